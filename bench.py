@@ -1,0 +1,185 @@
+"""Benchmark: ring exact attention forward on one MI355X.
+
+Workload (default): LV-XAttn-shaped cross-attention, batch 1, 32 heads,
+S_Q = 2048 text queries against S_KV = 131072 visual keys/values (one GPU's
+share), D = 128, bf16 inputs with fp32 accumulation, n = 8 KV shards.
+A step is one whole ring forward (every round of the schedule, every block
+pair, the merge and the final output) over inputs already resident in HBM.
+
+Prints one JSON line.  `value` is attention TFLOP/s counted as
+4 * B * H * S_Q * S_KV * D per step.  `roofline` reports the dominant kernel
+against the dense bf16 MFMA peak (2.5 PFLOP/s), its duration measured with
+HIP events on the stream the library launches on.  `cpu_baseline` times the
+fp64 CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention TFLOP/s and % bf16 MFMA peak, S_Q=2K x S_KV=128K d=128, 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_lvx_2k_128k_traffic.txt")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("fwd.hip", "common.h"):
+        with open(os.path.join(ROOT, "ring_exact_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(mode: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source and the same mode; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            a, b = line.split("=", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("kernel_hash") != kernel_source_hash() or kv.get("mode") != mode:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(q, k, v, w, rows_per_head: int):
+    import numpy as np
+
+    import oracle
+    g = np.random.default_rng(w.seed)
+    rows = []
+    for bh in range(w.B * w.H):
+        rows.extend(bh * w.SQ + g.choice(w.SQ, size=rows_per_head, replace=False))
+    rows = np.array(sorted(rows), dtype=np.int64)
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    t0 = time.perf_counter()
+    oracle.attn_fwd(qc, kc, vc, w.scale, causal=w.causal, rows=rows)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.SKV * w.D * len(rows)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{len(rows)} of {w.B * w.H * w.SQ} query rows ({rows_per_head} per head, "
+                      f"all {w.B * w.H} heads) against all {w.SKV} keys, fp64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="lvx_2k_128k")
+    ap.add_argument("--mode", default="fused", choices=["rounds", "fused", "split"])
+    ap.add_argument("--sched", default="kv", choices=["kv", "q"])
+    ap.add_argument("--cpu-rows-per-head", type=int, default=96)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only (the n ring workers are n KV shards "
+              "on one device); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import ring_exact_attention_amd as bwa
+    from ring_exact_attention_amd import _bwa
+    from ring_exact_attention_amd.inputs import WORKLOADS, make_qkv
+
+    if not os.path.exists(_bwa.LIB_PATH):
+        from ring_exact_attention_amd import build as hip_build
+        hip_build.build()
+    bwa.lib()
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = make_qkv(w, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, w.SQ, dtype=torch.float32, device=dev)
+    nbytes = bwa.ring_fwd_workspace(q, k, w.n, args.mode)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        bwa.bwa_ring_fwd(q, k, v, w.n, args.sched, args.mode, causal=w.causal, scale=w.scale,
+                         o=o, lse=lse, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms = sum(per_step_ms) / len(per_step_ms)
+
+    if w.causal:
+        flops = 4.0 * w.B * w.H * w.D * w.SQ * (w.SQ + 1) / 2
+    else:
+        flops = 4.0 * w.B * w.H * w.SQ * w.SKV * w.D
+    tflops = flops / (ms * 1e-3) / 1e12
+
+    # Dominant kernel: in fused mode the step is one launch of the block-pair
+    # kernel; in rounds mode n launches (one per round) plus a small finalize;
+    # in split mode one launch plus the merge.  Per-launch flops are the
+    # step's flops divided by the launches of that kernel.
+    launches = w.n if args.mode == "rounds" else 1
+    achieved = (flops / launches) / ((ms * 1e-3) / launches) / 1e12
+    traffic = read_traffic(args.mode)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "kernel": "fwd_bf16_kernel<128,8>",
+                "launches_per_step": launches}
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "ms_per_step_min": round(min(per_step_ms), 4),
+        "ms_per_step_max": round(max(per_step_ms), 4),
+        "wall_s_timed": round(wall, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "S_Q": w.SQ, "S_KV": w.SKV, "D": w.D,
+                   "n_shards": w.n, "schedule": args.sched, "mode": args.mode,
+                   "causal": w.causal, "seed": w.seed},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(q, k, v, w, args.cpu_rows_per_head)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

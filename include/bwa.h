@@ -1,0 +1,203 @@
+/*
+ * bwa.h -- C ABI of the MI355X (gfx950) blockwise / ring exact-attention library.
+ *
+ * What it computes.  Exact attention O = softmax(scale * Q K^T) V, one query
+ * block against one key/value block at a time.  Each block pair yields a
+ * partial output and its row log-sum-exp; partials of successive KV blocks
+ * (the rounds of a ring) are combined by FlashAttention-style rescaling, so
+ * the merged result equals unblocked attention up to rounding.
+ *   - "LV-XAttn: Distributed Cross-Attention for Long Visual Inputs in
+ *     Multimodal Large Language Models" (Pith review), "What carries the
+ *     argument": KV blocks stay on their worker; the query block Q_i, the
+ *     partial output O_i and the softmax statistics L_i rotate; partial
+ *     outputs are rescaled as in FlashAttention.  Figure 3 caption
+ *     (Algorithm 1): inputs Q_i, K_i, V_i, state O_i, L_i, n rounds.
+ *   - "Ring Attention with Blockwise Transformers for Near-Infinite Context",
+ *     abstract: query blocks stay, key/value blocks travel the ring,
+ *     blockwise attention with no approximation.
+ * On one GPU the n ring workers are n shards of the sequence on one device;
+ * a round is a stream-ordered kernel launch and no data moves between GPUs.
+ *
+ * Conventions shared by every entry point.
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or keeps caller memory; scratch memory
+ *     is passed in as `workspace` (size from the *_workspace query).
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL is the default stream).  Arguments are validated on the host
+ *     before anything is enqueued: a non-OK status means nothing was enqueued
+ *     (except BWA_ERR_HIP, which reports a failed launch).
+ *   - Errors are return codes only: no exceptions, no abort.  The last
+ *     failing call's detail is kept per host thread (bwa_last_error()).
+ *   - Layout: a bwa_tensor is [B, H, S, D] with element strides sB, sH, sS
+ *     and unit stride along D (so [B, S, H, D] storage works by strides).
+ *     The base pointer must be 16-byte aligned and sB, sH, sS multiples of
+ *     16 bytes.  D must be 64 or 128.
+ *   - scale is the softmax scale (callers pass 1/sqrt(D)); it must be finite
+ *     and positive.  LSE values are fp32, natural log, scale included.
+ *     An empty set of visible keys gives (O = 0, LSE = -inf).
+ *   - causal is self-attention masking by position (key j visible to query
+ *     i iff j <= i) and requires S_Q == S_KV.
+ *   - Shards: a length-S sequence split n ways has shard k =
+ *     [floor(k*S/n), floor((k+1)*S/n)).  Query blocks and KV shards use the
+ *     same split.  Round r pairs for virtual worker w:
+ *       BWA_SCHED_KV_STATIONARY (LV-XAttn): Q block (w - r) mod n, KV shard w;
+ *       BWA_SCHED_Q_STATIONARY  (Ring):     Q block w, KV shard (w - r) mod n.
+ *     Every round is a perfect matching and the n rounds cover all n^2
+ *     pairs.  Query block j therefore merges KV shards in the order
+ *     j, j+1, ... (KV-stationary) or j, j-1, ... (Q-stationary), mod n.
+ *   - Thread safety: no mutable global state; calls on different streams
+ *     may run concurrently if their output buffers are disjoint.
+ */
+#ifndef BWA_H_
+#define BWA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BWA_VERSION 1
+
+typedef enum {
+  BWA_OK = 0,
+  BWA_ERR_INVALID_ARG = 1, /* null pointer, bad shape, mismatched operands */
+  BWA_ERR_UNSUPPORTED = 2, /* valid but not implemented (dtype, D, alignment) */
+  BWA_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or too small */
+  BWA_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  BWA_ERR_INTERNAL = 5
+} bwa_status;
+
+typedef enum { BWA_F32 = 0, BWA_BF16 = 1 } bwa_dtype;
+
+typedef enum {
+  BWA_SCHED_KV_STATIONARY = 0, /* LV-XAttn: KV stays, Q/O/L rotate */
+  BWA_SCHED_Q_STATIONARY = 1   /* Ring Attention: Q stays, K/V rotate */
+} bwa_schedule;
+
+/*
+ * How the n rounds run on the one GPU.  All three compute the same n^2 block
+ * pairs and merge each query block's partials in its schedule's order; they
+ * differ only in fp32 rounding.
+ *   ROUNDS: n launches, one per round, each the round's n pairs; the running
+ *           (O, L) of every query block lives in fp32 between rounds.
+ *   FUSED:  one launch; each workgroup walks its query block's KV shards in
+ *           schedule order, carrying the softmax state in registers.
+ *   SPLIT:  one launch computes every pair's partial into the workspace,
+ *           then one merge launch combines them in schedule order.
+ */
+typedef enum { BWA_MODE_ROUNDS = 0, BWA_MODE_FUSED = 1, BWA_MODE_SPLIT = 2 } bwa_mode;
+
+typedef struct bwa_tensor {
+  void* ptr;       /* device pointer, 16-byte aligned */
+  int32_t dtype;   /* bwa_dtype */
+  int32_t reserved;
+  int64_t B, H, S, D;
+  int64_t sB, sH, sS; /* element strides; stride along D is 1 */
+} bwa_tensor;
+
+/*
+ * One block pair: query rows [q0, q0+nq) attend to key/value rows
+ * [k0, k0+nk) of every (batch, head).  (LV-XAttn review, "What carries the
+ * argument": the block attention of the query block a worker holds against
+ * its local KV block, rescaled as in FlashAttention.)
+ *   o_acc   fp32 [B, H, S_Q, D] contiguous: running normalised output.
+ *   lse_acc fp32 [B, H, S_Q]: running log-sum-exp.
+ *   accumulate = 0: rows [q0, q0+nq) are overwritten with this pair's
+ *                   partial (O_p, L_p);
+ *   accumulate = 1: the partial is rescale-merged into the rows' running
+ *                   (O, L) (the identity is O = 0, L = -inf).
+ * Other rows are not touched.  causal masks by global position
+ * (key k0+j visible to query q0+i iff k0+j <= q0+i).
+ * q, k, v share one dtype (fp32 or bf16).
+ */
+bwa_status bwa_partial_fwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v,
+                           int64_t q0, int64_t nq, int64_t k0, int64_t nk, float scale,
+                           int causal, float* o_acc, float* lse_acc, int accumulate,
+                           void* stream);
+
+/*
+ * Rescale-merge of two partials over disjoint key sets, row by row
+ * (LV-XAttn review, "What carries the argument" and "Assumptions": the
+ * online-softmax rescaling of partial O and L is exact):
+ *   M = max(L_a, L_b),  L = M + ln(e^(L_a - M) + e^(L_b - M)),
+ *   O = e^(L_a - L) O_a + e^(L_b - L) O_b;   (0, -inf) is the identity.
+ * o_* fp32 [rows, D] contiguous, lse_* fp32 [rows].  Outputs may alias
+ * either input exactly (same pointer), not partially.
+ */
+bwa_status bwa_merge(int64_t rows, int64_t D, const float* o_a, const float* lse_a,
+                     const float* o_b, const float* lse_b, float* o_out, float* lse_out,
+                     void* stream);
+
+/* Bytes of workspace bwa_ring_fwd needs (0 if none); 0 also for invalid arguments. */
+size_t bwa_ring_fwd_workspace(const bwa_tensor* q, const bwa_tensor* k, int n, bwa_mode mode);
+
+/*
+ * The whole ring forward on one GPU: n KV shards and n query blocks, n
+ * rounds of the chosen schedule, every query block's partials merged in its
+ * schedule's order (LV-XAttn review, Figure 3 / Algorithm 1 and "What
+ * carries the argument"; Ring Attention abstract).
+ *   q [B, H, S_Q, D], k and v [B, H, S_KV, D], one dtype.
+ *   o   [B, H, S_Q, D] in q's dtype (any strides per the conventions).
+ *   lse fp32 [B, H, S_Q] contiguous.
+ *   1 <= n <= S_KV.  causal requires S_Q == S_KV.
+ *   workspace: device memory of at least bwa_ring_fwd_workspace() bytes,
+ *   256-byte aligned (may be NULL when that is 0).
+ */
+bwa_status bwa_ring_fwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v, int n,
+                        bwa_schedule sched, bwa_mode mode, int causal, float scale,
+                        const bwa_tensor* o, float* lse, void* workspace, size_t ws_bytes,
+                        void* stream);
+
+/* Bytes of workspace bwa_ring_bwd needs; 0 also for invalid arguments. */
+size_t bwa_ring_bwd_workspace(const bwa_tensor* q, const bwa_tensor* k, int n, bwa_mode mode);
+
+/*
+ * Exact gradient of the ring forward (LV-XAttn review, referee report major
+ * comment 1: the distributed backward must reproduce the gradient of the
+ * exact attention formula).  With P = exp(scale Q K^T - LSE):
+ *   dV = P^T dO,  dP = dO V^T,  Delta = rowsum(dO * O),
+ *   dS = P * (dP - Delta),  dQ = scale dS K,  dK = scale dS^T Q.
+ * Each block pair contributes additively, using the global LSE and Delta.
+ * KV-stationary: dK, dV stay with their shard while (Q, dO, LSE, Delta, dQ)
+ * rotate; Q-stationary: the reverse.  Modes as in bwa_ring_fwd (SPLIT is
+ * treated as FUSED).
+ *   o, dout [B, H, S_Q, D] and lse fp32 [B, H, S_Q] from the forward.
+ *   dq [B, H, S_Q, D], dk and dv [B, H, S_KV, D] in q's dtype (overwritten).
+ * Only bf16 with D = 128 is implemented (else BWA_ERR_UNSUPPORTED).
+ */
+bwa_status bwa_ring_bwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v,
+                        const bwa_tensor* o, const float* lse, const bwa_tensor* dout, int n,
+                        bwa_schedule sched, bwa_mode mode, int causal, float scale,
+                        const bwa_tensor* dq, const bwa_tensor* dk, const bwa_tensor* dv,
+                        void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Recompute of keys and values from the one shared copy of the visual
+ * features (LV-XAttn review, "What carries the argument": all
+ * cross-attention layers read the same y, so only y is kept and K = y W_k,
+ * V = y W_v are recomputed when needed):
+ *   k[b, h, s, d] = sum_e y[b, s, e] * W_k[e, h*D + d], likewise v with W_v.
+ *   y     bf16 [B, S_KV, E] contiguous.
+ *   wk_t, wv_t bf16 [H*D, E] contiguous: W_k, W_v transposed (row n holds
+ *         column n of W), the [out, in] layout of a linear layer's weight.
+ *   k, v  bf16 [B, H, S_KV, D] tensors (any strides per the conventions).
+ * bf16 only; E must be a multiple of 64 and H*D a multiple of 128.
+ */
+bwa_status bwa_kv_recompute(const void* y, const void* wk_t, const void* wv_t, int64_t B,
+                            int64_t S_KV, int64_t E, int64_t H, int64_t D, int32_t dtype,
+                            const bwa_tensor* k, const bwa_tensor* v, void* stream);
+
+/* Static string naming a status code. */
+const char* bwa_status_string(bwa_status s);
+/* Detail of the calling thread's last failing call ("" if none). */
+const char* bwa_last_error(void);
+/* BWA_VERSION of the built library. */
+int bwa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BWA_H_ */

@@ -1,0 +1,236 @@
+"""ctypes binding of libbwa.so (the C ABI in include/bwa.h).
+
+Argument marshalling only: tensors become (pointer, shape, strides) records,
+the current torch stream becomes the hipStream_t, and PyTorch allocates the
+outputs and workspace.  Every step of the computation runs in the library's
+HIP kernels; there is no fallback.  If the library is not built, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbwa.so")
+
+BWA_OK, BWA_ERR_INVALID_ARG, BWA_ERR_UNSUPPORTED, BWA_ERR_WORKSPACE, BWA_ERR_HIP, \
+    BWA_ERR_INTERNAL = range(6)
+BWA_F32, BWA_BF16 = 0, 1
+SCHED_KV_STATIONARY, SCHED_Q_STATIONARY = 0, 1
+MODE_ROUNDS, MODE_FUSED, MODE_SPLIT = 0, 1, 2
+
+SCHEDULES = {"kv": SCHED_KV_STATIONARY, "lv": SCHED_KV_STATIONARY, "kv_stationary": 0,
+             "q": SCHED_Q_STATIONARY, "ring": SCHED_Q_STATIONARY, "q_stationary": 1}
+MODES = {"rounds": MODE_ROUNDS, "fused": MODE_FUSED, "split": MODE_SPLIT}
+
+EXPORTED = ("bwa_partial_fwd", "bwa_merge", "bwa_ring_fwd_workspace", "bwa_ring_fwd",
+            "bwa_ring_bwd_workspace", "bwa_ring_bwd", "bwa_kv_recompute", "bwa_status_string",
+            "bwa_last_error", "bwa_version")
+
+
+class BwaError(RuntimeError):
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__(f"{name}: {detail}")
+        self.status = status
+
+
+class Tensor(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("S", ctypes.c_int64),
+                ("D", ctypes.c_int64), ("sB", ctypes.c_int64), ("sH", ctypes.c_int64),
+                ("sS", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m "
+                               "ring_exact_attention_amd.build` (or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, f32, ci, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int,
+                                ctypes.c_size_t)
+        T = ctypes.POINTER(Tensor)
+        L.bwa_partial_fwd.argtypes = [T, T, T, i64, i64, i64, i64, f32, ci, vp, vp, ci, vp]
+        L.bwa_merge.argtypes = [i64, i64, vp, vp, vp, vp, vp, vp, vp]
+        L.bwa_ring_fwd_workspace.argtypes = [T, T, ci, ci]
+        L.bwa_ring_fwd_workspace.restype = sz
+        L.bwa_ring_fwd.argtypes = [T, T, T, ci, ci, ci, ci, f32, T, vp, vp, sz, vp]
+        L.bwa_ring_bwd_workspace.argtypes = [T, T, ci, ci]
+        L.bwa_ring_bwd_workspace.restype = sz
+        L.bwa_ring_bwd.argtypes = [T, T, T, T, vp, T, ci, ci, ci, ci, f32, T, T, T, vp, sz, vp]
+        L.bwa_kv_recompute.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int32, T, T,
+                                       vp]
+        for name in ("bwa_partial_fwd", "bwa_merge", "bwa_ring_fwd", "bwa_ring_bwd",
+                     "bwa_kv_recompute"):
+            getattr(L, name).restype = ci
+        L.bwa_status_string.argtypes = [ci]
+        L.bwa_status_string.restype = ctypes.c_char_p
+        L.bwa_last_error.restype = ctypes.c_char_p
+        L.bwa_version.restype = ci
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != BWA_OK:
+        L = lib()
+        raise BwaError(status, L.bwa_status_string(status).decode(),
+                       L.bwa_last_error().decode())
+
+
+def _dtype_code(dt) -> int:
+    if dt == torch.bfloat16:
+        return BWA_BF16
+    if dt == torch.float32:
+        return BWA_F32
+    raise TypeError(f"dtype {dt} not supported (float32, bfloat16)")
+
+
+def as_bwa(t: torch.Tensor) -> Tensor:
+    """Describe a [B, H, S, D] device tensor (unit stride along D) to the library."""
+    _on_device(t)
+    if t.dim() != 4:
+        raise ValueError("expected a [B, H, S, D] tensor")
+    if t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError("the head dimension must have unit stride")
+    B, H, S, D = t.shape
+    sB, sH, sS, _ = t.stride()
+    return Tensor(t.data_ptr() if t.numel() else 0, _dtype_code(t.dtype), 0, B, H, S, D, sB, sH,
+                  sS)
+
+
+def _on_device(t: torch.Tensor):
+    if not t.is_cuda:
+        raise ValueError("tensors must live in GPU memory (the library takes device pointers)")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    _on_device(t)
+    return t.data_ptr()
+
+
+def bwa_partial_fwd(q, k, v, q0, nq, k0, nk, scale, causal, o_acc, lse_acc, accumulate):
+    """One block pair merged into (o_acc fp32 [B,H,SQ,D], lse_acc fp32 [B,H,SQ])."""
+    for name, t in (("o_acc", o_acc), ("lse_acc", lse_acc)):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous float32")
+    tq, tk, tv = as_bwa(q), as_bwa(k), as_bwa(v)
+    _check(lib().bwa_partial_fwd(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), q0, nq, k0,
+                                 nk, float(scale), int(bool(causal)), _ptr(o_acc), _ptr(lse_acc),
+                                 int(bool(accumulate)), _stream(q.device)))
+
+
+def bwa_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None):
+    """Rescale-merge two fp32 partials ([..., D], [...]); returns (o_out, lse_out)."""
+    for t in (o_a, lse_a, o_b, lse_b):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("merge inputs must be contiguous float32")
+    o_out = torch.empty_like(o_a) if o_out is None else o_out
+    lse_out = torch.empty_like(lse_a) if lse_out is None else lse_out
+    D = o_a.shape[-1]
+    rows = lse_a.numel()
+    if o_a.numel() != rows * D or o_b.shape != o_a.shape or lse_b.shape != lse_a.shape:
+        raise ValueError("merge operand shapes differ")
+    _check(lib().bwa_merge(rows, D, _ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o_out),
+                           _ptr(lse_out), _stream(o_a.device)))
+    return o_out, lse_out
+
+
+def _sched(s) -> int:
+    return SCHEDULES[s] if isinstance(s, str) else int(s)
+
+
+def _mode(m) -> int:
+    return MODES[m] if isinstance(m, str) else int(m)
+
+
+def ring_fwd_workspace(q, k, n, mode) -> int:
+    tq, tk = as_bwa(q), as_bwa(k)
+    return int(lib().bwa_ring_fwd_workspace(ctypes.byref(tq), ctypes.byref(tk), n, _mode(mode)))
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0:
+        return None
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace smaller than {nbytes} bytes")
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def bwa_ring_fwd(q, k, v, n, sched="kv", mode="fused", causal=False, scale=None, o=None,
+                 lse=None, workspace=None):
+    """Ring forward over n shards; returns (o [B,H,SQ,D] q.dtype, lse fp32 [B,H,SQ])."""
+    B, H, SQ, D = q.shape
+    scale = D ** -0.5 if scale is None else scale
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty(B, H, SQ, dtype=torch.float32, device=q.device) if lse is None else lse
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32")
+    m = _mode(mode)
+    ws = _workspace(ring_fwd_workspace(q, k, n, m), q.device, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    tq, tk, tv, to = as_bwa(q), as_bwa(k), as_bwa(v), as_bwa(o)
+    _check(lib().bwa_ring_fwd(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), int(n),
+                              _sched(sched), m, int(bool(causal)), float(scale), ctypes.byref(to),
+                              _ptr(lse), _ptr(ws), nbytes, _stream(q.device)))
+    return o, lse
+
+
+def ring_bwd_workspace(q, k, n, mode) -> int:
+    tq, tk = as_bwa(q), as_bwa(k)
+    return int(lib().bwa_ring_bwd_workspace(ctypes.byref(tq), ctypes.byref(tk), n, _mode(mode)))
+
+
+def bwa_ring_bwd(q, k, v, o, lse, dout, n, sched="kv", mode="fused", causal=False, scale=None,
+                 dq=None, dk=None, dv=None, workspace=None):
+    """Ring backward; returns (dq, dk, dv) in q's dtype."""
+    D = q.shape[-1]
+    scale = D ** -0.5 if scale is None else scale
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32")
+    m = _mode(mode)
+    ws = _workspace(ring_bwd_workspace(q, k, n, m), q.device, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    t = [as_bwa(x) for x in (q, k, v, o, dout, dq, dk, dv)]
+    _check(lib().bwa_ring_bwd(ctypes.byref(t[0]), ctypes.byref(t[1]), ctypes.byref(t[2]),
+                              ctypes.byref(t[3]), _ptr(lse), ctypes.byref(t[4]), int(n),
+                              _sched(sched), m, int(bool(causal)), float(scale),
+                              ctypes.byref(t[5]), ctypes.byref(t[6]), ctypes.byref(t[7]),
+                              _ptr(ws), nbytes, _stream(q.device)))
+    return dq, dk, dv
+
+
+def bwa_kv_recompute(y, wk_t, wv_t, H, D, k=None, v=None):
+    """K = y W_k, V = y W_v (W given transposed, [H*D, E]); returns (k, v) [B,H,S,D] bf16."""
+    B, S, E = y.shape
+    for name, t in (("y", y), ("wk_t", wk_t), ("wv_t", wv_t)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k is None:
+        k = torch.empty(B, H, S, D, dtype=y.dtype, device=y.device)
+    if v is None:
+        v = torch.empty(B, H, S, D, dtype=y.dtype, device=y.device)
+    tk, tv = as_bwa(k), as_bwa(v)
+    _check(lib().bwa_kv_recompute(_ptr(y), _ptr(wk_t), _ptr(wv_t), B, S, E, H, D,
+                                  _dtype_code(y.dtype), ctypes.byref(tk), ctypes.byref(tv),
+                                  _stream(y.device)))
+    return k, v

@@ -1,0 +1,353 @@
+// Host side of the C ABI declared in include/bwa.h: argument validation,
+// workspace carving, and the stream-ordered round loop that stands in for the
+// ring on one GPU.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "bwa.h"
+#include "bwd_args.h"
+#include "common.h"
+
+namespace bwa {
+hipError_t fwd_launch(FwdParams p, int dtype_bf16, hipStream_t st);
+int fwd_tile_rows(int dtype_bf16, int D);
+hipError_t merge2_launch(int64_t rows, int D, const float* oa, const float* la, const float* ob,
+                         const float* lb, float* oo, float* lo, hipStream_t st);
+hipError_t split_merge_launch(FwdParams p, int dtype_bf16, hipStream_t st);
+hipError_t finalize_launch(FwdParams p, int dtype_bf16, hipStream_t st);
+bool bwd_supported(int dtype, int D);
+size_t bwd_workspace_bytes(int64_t BH, int64_t SQ, int64_t SKV, int D, int n, int mode);
+hipError_t bwd_run(const BwdArgs& a, hipStream_t st);
+hipError_t gemm_kv_launch(const void* y, const void* wk_t, const void* wv_t, int64_t B, int64_t S,
+                          int64_t E, int64_t H, int64_t D, const bwa_tensor* k,
+                          const bwa_tensor* v, hipStream_t st);
+}  // namespace bwa
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bwa_status fail(bwa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+bwa_status hip_fail(hipError_t e, const char* what) {
+  return fail(BWA_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+size_t elem_size(int32_t dt) { return dt == BWA_BF16 ? 2 : 4; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+// Structural checks shared by every tensor argument.
+bwa_status check_tensor(const bwa_tensor* t, const char* name, bool allow_empty_seq) {
+  if (!t) return fail(BWA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (t->dtype != BWA_F32 && t->dtype != BWA_BF16)
+    return fail(BWA_ERR_UNSUPPORTED, "%s: dtype %d not supported (fp32=0, bf16=1)", name,
+                (int)t->dtype);
+  if (t->B <= 0 || t->H <= 0 || t->S < 0 || (t->S == 0 && !allow_empty_seq))
+    return fail(BWA_ERR_INVALID_ARG, "%s: bad shape B=%lld H=%lld S=%lld", name,
+                (long long)t->B, (long long)t->H, (long long)t->S);
+  if (t->D != 64 && t->D != 128)
+    return fail(BWA_ERR_UNSUPPORTED, "%s: head dim %lld not supported (64 or 128)", name,
+                (long long)t->D);
+  if (t->B * t->H >= kMaxDim || t->S >= kMaxDim)
+    return fail(BWA_ERR_UNSUPPORTED, "%s: sizes beyond 2^31 rows", name);
+  if (t->sB < 0 || t->sH < 0 || t->sS < 0)
+    return fail(BWA_ERR_INVALID_ARG, "%s: negative stride", name);
+  if (t->S == 0) return BWA_OK;
+  if (!t->ptr) return fail(BWA_ERR_INVALID_ARG, "%s: NULL data pointer", name);
+  size_t es = elem_size(t->dtype);
+  if ((uintptr_t)t->ptr % 16 != 0 || (t->sB * es) % 16 != 0 || (t->sH * es) % 16 != 0 ||
+      (t->sS * es) % 16 != 0)
+    return fail(BWA_ERR_UNSUPPORTED, "%s: base and strides must be 16-byte aligned", name);
+  return BWA_OK;
+}
+
+bwa_status check_qkv(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v, int causal) {
+  bwa_status s;
+  if ((s = check_tensor(q, "q", true)) != BWA_OK) return s;
+  if ((s = check_tensor(k, "k", false)) != BWA_OK) return s;
+  if ((s = check_tensor(v, "v", false)) != BWA_OK) return s;
+  if (q->dtype != k->dtype || q->dtype != v->dtype)
+    return fail(BWA_ERR_INVALID_ARG, "q, k, v must share one dtype");
+  if (q->B != k->B || q->B != v->B || q->H != k->H || q->H != v->H)
+    return fail(BWA_ERR_INVALID_ARG, "q, k, v batch/head counts differ");
+  if (q->D != k->D || q->D != v->D) return fail(BWA_ERR_INVALID_ARG, "q, k, v head dims differ");
+  if (k->S != v->S) return fail(BWA_ERR_INVALID_ARG, "k and v lengths differ");
+  if (causal && q->S != k->S)
+    return fail(BWA_ERR_UNSUPPORTED, "causal masking needs S_Q == S_KV (self-attention)");
+  return BWA_OK;
+}
+
+bwa_status check_like(const bwa_tensor* t, const bwa_tensor* ref, int64_t S, const char* name) {
+  bwa_status s = check_tensor(t, name, true);
+  if (s != BWA_OK) return s;
+  if (t->dtype != ref->dtype || t->B != ref->B || t->H != ref->H || t->S != S || t->D != ref->D)
+    return fail(BWA_ERR_INVALID_ARG, "%s: shape or dtype does not match", name);
+  return BWA_OK;
+}
+
+bwa_status check_scale(float scale) {
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(BWA_ERR_INVALID_ARG, "scale must be finite and positive");
+  return BWA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t fwd_ws_bytes(int64_t BH, int64_t SQ, int D, int n, int mode) {
+  if (mode == BWA_MODE_ROUNDS) return align256((size_t)(BH * SQ * D) * 4);
+  if (mode == BWA_MODE_SPLIT)
+    return align256((size_t)n * BH * SQ * D * 4) + align256((size_t)n * BH * SQ * 4);
+  return 0;
+}
+
+bwa::FwdParams base_params(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v,
+                           float scale, int causal) {
+  bwa::FwdParams p = {};
+  p.q = q->ptr;
+  p.k = k->ptr;
+  p.v = v->ptr;
+  p.sqB = q->sB; p.sqH = q->sH; p.sqS = q->sS;
+  p.skB = k->sB; p.skH = k->sH; p.skS = k->sS;
+  p.svB = v->sB; p.svH = v->sH; p.svS = v->sS;
+  p.B = (int)q->B;
+  p.H = (int)q->H;
+  p.SQ = (int)q->S;
+  p.SKV = (int)k->S;
+  p.D = (int)q->D;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  p.scale_log2 = scale * bwa::kLog2e;
+  return p;
+}
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+bwa_status check_ring(const bwa_tensor* q, const bwa_tensor* k, int n, int mode) {
+  if (n < 1 || n > k->S)
+    return fail(BWA_ERR_INVALID_ARG, "n = %d shards must be in [1, S_KV = %lld]", n,
+                (long long)k->S);
+  if (n > 4096) return fail(BWA_ERR_UNSUPPORTED, "n = %d above 4096", n);
+  if (mode != BWA_MODE_ROUNDS && mode != BWA_MODE_FUSED && mode != BWA_MODE_SPLIT)
+    return fail(BWA_ERR_INVALID_ARG, "unknown mode %d", mode);
+  (void)q;
+  return BWA_OK;
+}
+
+bwa_status check_sched(int sched) {
+  if (sched != BWA_SCHED_KV_STATIONARY && sched != BWA_SCHED_Q_STATIONARY)
+    return fail(BWA_ERR_INVALID_ARG, "unknown schedule %d", sched);
+  return BWA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bwa_status_string(bwa_status s) {
+  switch (s) {
+    case BWA_OK: return "BWA_OK";
+    case BWA_ERR_INVALID_ARG: return "BWA_ERR_INVALID_ARG";
+    case BWA_ERR_UNSUPPORTED: return "BWA_ERR_UNSUPPORTED";
+    case BWA_ERR_WORKSPACE: return "BWA_ERR_WORKSPACE";
+    case BWA_ERR_HIP: return "BWA_ERR_HIP";
+    case BWA_ERR_INTERNAL: return "BWA_ERR_INTERNAL";
+  }
+  return "BWA_ERR_UNKNOWN";
+}
+
+const char* bwa_last_error(void) { return g_last_error.c_str(); }
+
+int bwa_version(void) { return BWA_VERSION; }
+
+bwa_status bwa_partial_fwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v,
+                           int64_t q0, int64_t nq, int64_t k0, int64_t nk, float scale,
+                           int causal, float* o_acc, float* lse_acc, int accumulate,
+                           void* stream) {
+  bwa_status s;
+  if ((s = check_qkv(q, k, v, causal)) != BWA_OK) return s;
+  if ((s = check_scale(scale)) != BWA_OK) return s;
+  if (q0 < 0 || nq < 0 || q0 + nq > q->S)
+    return fail(BWA_ERR_INVALID_ARG, "query range [%lld, %lld) outside [0, %lld)",
+                (long long)q0, (long long)(q0 + nq), (long long)q->S);
+  if (k0 < 0 || nk < 0 || k0 + nk > k->S)
+    return fail(BWA_ERR_INVALID_ARG, "key range [%lld, %lld) outside [0, %lld)", (long long)k0,
+                (long long)(k0 + nk), (long long)k->S);
+  if (nq == 0) return BWA_OK;
+  if (!o_acc || !lse_acc) return fail(BWA_ERR_INVALID_ARG, "o_acc / lse_acc is NULL");
+  if ((uintptr_t)o_acc % 16 != 0) return fail(BWA_ERR_UNSUPPORTED, "o_acc must be 16-byte aligned");
+  bwa::FwdParams p = base_params(q, k, v, scale, causal);
+  p.single_pair = 1;
+  p.q0 = q0; p.nq = nq; p.k0 = k0; p.nk = nk;
+  p.accumulate = accumulate ? 1 : 0;
+  p.o_acc = o_acc;
+  p.lse = lse_acc;
+  p.mode = bwa::MODE_ROUNDS;
+  p.n = 1;
+  const int bf = q->dtype == BWA_BF16;
+  p.tiles = ceil_div(nq, bwa::fwd_tile_rows(bf, p.D));
+  p.groups = p.B * p.H;
+  hipError_t e = bwa::fwd_launch(p, bf, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "partial forward launch");
+  return BWA_OK;
+}
+
+bwa_status bwa_merge(int64_t rows, int64_t D, const float* o_a, const float* lse_a,
+                     const float* o_b, const float* lse_b, float* o_out, float* lse_out,
+                     void* stream) {
+  if (rows < 0) return fail(BWA_ERR_INVALID_ARG, "rows < 0");
+  if (D != 64 && D != 128) return fail(BWA_ERR_UNSUPPORTED, "D must be 64 or 128");
+  if (rows == 0) return BWA_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b || !o_out || !lse_out)
+    return fail(BWA_ERR_INVALID_ARG, "NULL pointer argument");
+  if ((uintptr_t)o_a % 16 || (uintptr_t)o_b % 16 || (uintptr_t)o_out % 16)
+    return fail(BWA_ERR_UNSUPPORTED, "O buffers must be 16-byte aligned");
+  hipError_t e = bwa::merge2_launch(rows, (int)D, o_a, lse_a, o_b, lse_b, o_out, lse_out,
+                                    (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return BWA_OK;
+}
+
+size_t bwa_ring_fwd_workspace(const bwa_tensor* q, const bwa_tensor* k, int n, bwa_mode mode) {
+  if (!q || !k || q->B <= 0 || q->H <= 0 || q->S < 0 || (q->D != 64 && q->D != 128) || n < 1)
+    return 0;
+  return fwd_ws_bytes(q->B * q->H, q->S, (int)q->D, n, mode);
+}
+
+bwa_status bwa_ring_fwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v, int n,
+                        bwa_schedule sched, bwa_mode mode, int causal, float scale,
+                        const bwa_tensor* o, float* lse, void* workspace, size_t ws_bytes,
+                        void* stream) {
+  bwa_status s;
+  if ((s = check_qkv(q, k, v, causal)) != BWA_OK) return s;
+  if ((s = check_like(o, q, q->S, "o")) != BWA_OK) return s;
+  if ((s = check_scale(scale)) != BWA_OK) return s;
+  if ((s = check_ring(q, k, n, mode)) != BWA_OK) return s;
+  if ((s = check_sched(sched)) != BWA_OK) return s;
+  if (q->S == 0) return BWA_OK;
+  if (!lse) return fail(BWA_ERR_INVALID_ARG, "lse is NULL");
+  const int64_t BH = q->B * q->H;
+  size_t need = fwd_ws_bytes(BH, q->S, (int)q->D, n, mode);
+  if (need > 0) {
+    if (!workspace || ws_bytes < need)
+      return fail(BWA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    if ((uintptr_t)workspace % 256 != 0)
+      return fail(BWA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  bwa::FwdParams p = base_params(q, k, v, scale, causal);
+  p.n = n;
+  p.sched = sched;
+  p.mode = mode;
+  p.o = o->ptr;
+  p.soB = o->sB; p.soH = o->sH; p.soS = o->sS;
+  p.lse = lse;
+  const int bf = q->dtype == BWA_BF16;
+  const int BM = bwa::fwd_tile_rows(bf, p.D);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  p.groups = (int)(BH * n);
+  if (mode == BWA_MODE_ROUNDS) {
+    p.o_acc = (float*)workspace;
+    p.tiles = ceil_div(ceil_div(q->S, n), BM);
+    for (int r = 0; r < n && e == hipSuccess; ++r) {
+      p.round = r;
+      e = bwa::fwd_launch(p, bf, st);
+    }
+    if (e == hipSuccess) e = bwa::finalize_launch(p, bf, st);
+  } else if (mode == BWA_MODE_FUSED) {
+    p.tiles = ceil_div(ceil_div(q->S, n), BM);
+    e = bwa::fwd_launch(p, bf, st);
+  } else {
+    p.o_acc = (float*)workspace;
+    p.lse_part = (float*)((char*)workspace + align256((size_t)n * BH * q->S * q->D * 4));
+    p.tiles = ceil_div(q->S, BM);
+    e = bwa::fwd_launch(p, bf, st);
+    if (e == hipSuccess) e = bwa::split_merge_launch(p, bf, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "ring forward launch");
+  return BWA_OK;
+}
+
+size_t bwa_ring_bwd_workspace(const bwa_tensor* q, const bwa_tensor* k, int n, bwa_mode mode) {
+  if (!q || !k || q->B <= 0 || q->H <= 0 || q->S < 0 || k->S < 0 ||
+      (q->D != 64 && q->D != 128) || n < 1)
+    return 0;
+  return bwa::bwd_workspace_bytes(q->B * q->H, q->S, k->S, (int)q->D, n, mode);
+}
+
+bwa_status bwa_ring_bwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v,
+                        const bwa_tensor* o, const float* lse, const bwa_tensor* dout, int n,
+                        bwa_schedule sched, bwa_mode mode, int causal, float scale,
+                        const bwa_tensor* dq, const bwa_tensor* dk, const bwa_tensor* dv,
+                        void* workspace, size_t ws_bytes, void* stream) {
+  bwa_status s;
+  if ((s = check_qkv(q, k, v, causal)) != BWA_OK) return s;
+  if ((s = check_like(o, q, q->S, "o")) != BWA_OK) return s;
+  if ((s = check_like(dout, q, q->S, "dout")) != BWA_OK) return s;
+  if ((s = check_like(dq, q, q->S, "dq")) != BWA_OK) return s;
+  if ((s = check_like(dk, q, k->S, "dk")) != BWA_OK) return s;
+  if ((s = check_like(dv, q, k->S, "dv")) != BWA_OK) return s;
+  if ((s = check_scale(scale)) != BWA_OK) return s;
+  if ((s = check_ring(q, k, n, mode)) != BWA_OK) return s;
+  if ((s = check_sched(sched)) != BWA_OK) return s;
+  if (!bwa::bwd_supported(q->dtype, (int)q->D))
+    return fail(BWA_ERR_UNSUPPORTED, "backward implemented for bf16, D = 128 only");
+  if (q->S == 0) return BWA_OK;
+  if (!lse) return fail(BWA_ERR_INVALID_ARG, "lse is NULL");
+  const int64_t BH = q->B * q->H;
+  size_t need = bwa::bwd_workspace_bytes(BH, q->S, k->S, (int)q->D, n, mode);
+  if (need > 0) {
+    if (!workspace || ws_bytes < need)
+      return fail(BWA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    if ((uintptr_t)workspace % 256 != 0)
+      return fail(BWA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  bwa::BwdArgs a = {};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
+  a.lse = lse;
+  a.n = n;
+  a.sched = sched;
+  a.mode = mode;
+  a.causal = causal ? 1 : 0;
+  a.scale = scale;
+  a.workspace = workspace;
+  hipError_t e = bwa::bwd_run(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "ring backward launch");
+  return BWA_OK;
+}
+
+bwa_status bwa_kv_recompute(const void* y, const void* wk_t, const void* wv_t, int64_t B,
+                            int64_t S_KV, int64_t E, int64_t H, int64_t D, int32_t dtype,
+                            const bwa_tensor* k, const bwa_tensor* v, void* stream) {
+  if (dtype != BWA_BF16) return fail(BWA_ERR_UNSUPPORTED, "kv_recompute is bf16 only");
+  if (B <= 0 || S_KV < 0 || E <= 0 || H <= 0) return fail(BWA_ERR_INVALID_ARG, "bad sizes");
+  if (D != 64 && D != 128) return fail(BWA_ERR_UNSUPPORTED, "D must be 64 or 128");
+  if (E % 64 != 0) return fail(BWA_ERR_UNSUPPORTED, "E must be a multiple of 64");
+  if ((H * D) % 128 != 0) return fail(BWA_ERR_UNSUPPORTED, "H*D must be a multiple of 128");
+  if (B * S_KV >= kMaxDim || E >= kMaxDim) return fail(BWA_ERR_UNSUPPORTED, "sizes too large");
+  bwa_status s;
+  if ((s = check_tensor(k, "k", true)) != BWA_OK) return s;
+  if ((s = check_tensor(v, "v", true)) != BWA_OK) return s;
+  if (k->dtype != BWA_BF16 || v->dtype != BWA_BF16 || k->B != B || v->B != B || k->H != H ||
+      v->H != H || k->S != S_KV || v->S != S_KV || k->D != D || v->D != D)
+    return fail(BWA_ERR_INVALID_ARG, "k / v shape or dtype does not match [B, H, S_KV, D] bf16");
+  if (S_KV == 0) return BWA_OK;
+  if (!y || !wk_t || !wv_t) return fail(BWA_ERR_INVALID_ARG, "NULL input pointer");
+  if ((uintptr_t)y % 16 || (uintptr_t)wk_t % 16 || (uintptr_t)wv_t % 16)
+    return fail(BWA_ERR_UNSUPPORTED, "y, wk_t, wv_t must be 16-byte aligned");
+  hipError_t e = bwa::gemm_kv_launch(y, wk_t, wv_t, B, S_KV, E, H, D, k, v, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kv recompute launch");
+  return BWA_OK;
+}
+
+}  // extern "C"

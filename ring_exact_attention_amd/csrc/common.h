@@ -1,0 +1,183 @@
+// Internal definitions shared by the HIP kernels and the host-side API.
+// Target: gfx950 (CDNA4) only, wave64.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bwa {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
+
+enum Mode { MODE_ROUNDS = 0, MODE_FUSED = 1, MODE_SPLIT = 2 };
+enum Sched { SCHED_KV_STATIONARY = 0, SCHED_Q_STATIONARY = 1 };
+enum Epilogue { EPI_FINAL = 0, EPI_ACC = 1, EPI_PART = 2 };
+
+// Start of shard k of a length-S sequence split n ways: floor(k*S/n).
+__host__ __device__ inline int64_t shard_start(int64_t S, int n, int k) {
+  return (int64_t)k * S / n;
+}
+
+// Pair held by virtual worker w in round r.
+//   KV-stationary: Q block (w - r) mod n with KV shard w.
+//   Q-stationary:  Q block w with KV shard (w - r) mod n.
+__host__ __device__ inline void ring_pair(int sched, int n, int r, int w, int* qb, int* kb) {
+  int moved = ((w - r) % n + n) % n;
+  if (sched == SCHED_KV_STATIONARY) { *qb = moved; *kb = w; }
+  else { *qb = w; *kb = moved; }
+}
+
+// KV shard merged into query block j at step r of its schedule order:
+// KV-stationary visits j, j+1, ...; Q-stationary visits j, j-1, ... (mod n).
+__host__ __device__ inline int shard_at_step(int sched, int n, int j, int r) {
+  return sched == SCHED_KV_STATIONARY ? (j + r) % n : ((j - r) % n + n) % n;
+}
+
+// Forward launch description (one struct for every mode and dtype).
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t sqB, sqH, sqS;
+  int64_t skB, skH, skS;
+  int64_t svB, svH, svS;
+  void* o;  // EPI_FINAL output, q's dtype
+  int64_t soB, soH, soS;
+  float* lse;       // [B,H,SQ]: EPI_FINAL output / EPI_ACC running LSE
+  float* o_acc;     // EPI_ACC running O fp32 [B,H,SQ,D]; EPI_PART partial O [n][B,H,SQ,D]
+  float* lse_part;  // EPI_PART partial LSE [n][B,H,SQ]
+  int B, H, SQ, SKV, D, n;
+  int sched, mode, causal, round;
+  int tiles;   // query tiles per group
+  int groups;  // groups of tiles (each group shares one KV range at a time)
+  int accumulate;
+  int single_pair;  // bwa_partial_fwd: one explicit pair
+  int64_t q0, nq, k0, nk;
+  float scale;       // softmax scale
+  float scale_log2;  // scale * log2(e)
+};
+
+// A workgroup's job: one (batch*head, query row range) and the ordered list
+// of KV segments it attends to.
+struct Job {
+  int bh;
+  int64_t r0, r1;  // query rows [r0, r1)
+  int block;       // query block (ROUNDS, FUSED) or KV shard slot (SPLIT)
+  int kb;          // the one KV shard of a ROUNDS / SPLIT job
+  int nseg;        // number of segment steps
+  int epi;         // Epilogue
+  bool acc_in;     // EPI_ACC: seed from the running (O, L)
+};
+
+// XCD-aware mapping of a linear workgroup id to (group, tile).  Workgroups are
+// dispatched round-robin over the 8 XCDs (id % 8); the `tiles` workgroups of
+// one group share a KV range and land on one XCD with consecutive slots, so
+// they stream the same K/V tiles through that XCD's L2 at about the same time.
+__device__ inline bool xcd_group_tile(int wg, int tiles, int groups, int* g, int* t) {
+  int xcd = wg % kNumXcd;
+  int k = wg / kNumXcd;
+  *g = (k / tiles) * kNumXcd + xcd;
+  *t = k % tiles;
+  return *g < groups;
+}
+
+inline int xcd_grid_size(int tiles, int groups) {
+  return kNumXcd * tiles * ((groups + kNumXcd - 1) / kNumXcd);
+}
+
+__device__ inline bool make_job(const FwdParams& p, int BM, Job* jb) {
+  int g, t;
+  if (!xcd_group_tile(blockIdx.x, p.tiles, p.groups, &g, &t)) return false;
+  const int BH = p.B * p.H;
+  if (p.single_pair) {
+    jb->bh = g;
+    jb->r0 = p.q0 + (int64_t)t * BM;
+    jb->r1 = min(p.q0 + p.nq, jb->r0 + BM);
+    jb->block = 0;
+    jb->kb = 0;
+    jb->nseg = 1;
+    jb->epi = EPI_ACC;
+    jb->acc_in = p.accumulate != 0;
+    return jb->r0 < jb->r1;
+  }
+  if (p.mode == MODE_SPLIT) {
+    jb->bh = g % BH;
+    jb->block = g / BH;
+    jb->kb = jb->block;
+    jb->r0 = (int64_t)t * BM;
+    jb->r1 = min((int64_t)p.SQ, jb->r0 + BM);
+    jb->nseg = 1;
+    jb->epi = EPI_PART;
+    jb->acc_in = false;
+    return jb->r0 < jb->r1;
+  }
+  int j;
+  jb->bh = g % BH;
+  if (p.mode == MODE_ROUNDS) {
+    int kb;
+    ring_pair(p.sched, p.n, p.round, g / BH, &j, &kb);
+    jb->kb = kb;
+    jb->nseg = 1;
+    jb->epi = EPI_ACC;
+    jb->acc_in = p.round > 0;
+  } else {  // FUSED; under causal masking later query blocks do more work: start them first
+    j = p.causal ? (p.n - 1 - g / BH) : (g / BH);
+    jb->kb = -1;
+    jb->nseg = p.n;
+    jb->epi = EPI_FINAL;
+    jb->acc_in = false;
+  }
+  jb->block = j;
+  int64_t qs = shard_start(p.SQ, p.n, j), qe = shard_start(p.SQ, p.n, j + 1);
+  jb->r0 = qs + (int64_t)t * BM;
+  jb->r1 = min(qe, jb->r0 + BM);
+  return jb->r0 < jb->r1;
+}
+
+// KV segment [*k0, *k1) of step r of a job (empty when nothing is visible).
+// Under causal masking no key at or beyond the job's last row + 1 is visible.
+__device__ inline void job_segment(const FwdParams& p, const Job& jb, int r, int64_t* k0,
+                                   int64_t* k1) {
+  if (p.single_pair) {
+    *k0 = p.k0;
+    *k1 = p.k0 + p.nk;
+  } else {
+    int kb = jb.kb >= 0 ? jb.kb : shard_at_step(p.sched, p.n, jb.block, r);
+    *k0 = shard_start(p.SKV, p.n, kb);
+    *k1 = shard_start(p.SKV, p.n, kb + 1);
+  }
+  if (p.causal && *k1 > jb.r1) *k1 = jb.r1;
+  if (*k1 < *k0) *k1 = *k0;
+}
+
+// Iterates the KV tiles of a job in order: segment by segment, BN keys at a time.
+struct TileIter {
+  int r;           // segment step
+  int64_t kt, ke;  // current tile start, end of current segment
+  __device__ inline void seek(const FwdParams& p, const Job& jb, int from, int BN) {
+    (void)BN;
+    for (r = from; r < jb.nseg; ++r) {
+      int64_t a, b;
+      job_segment(p, jb, r, &a, &b);
+      if (b > a) { kt = a; ke = b; return; }
+    }
+    kt = ke = 0;
+  }
+  __device__ inline bool valid(const Job& jb) const { return r < jb.nseg; }
+  __device__ inline void advance(const FwdParams& p, const Job& jb, int BN) {
+    kt += BN;
+    if (kt >= ke) seek(p, jb, r + 1, BN);
+  }
+};
+
+}  // namespace bwa

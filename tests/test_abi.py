@@ -1,0 +1,177 @@
+"""C-ABI library: loads, exports every declared symbol, validates arguments.
+
+No compute call is made here (there is no GPU in this suite): every call
+below fails validation on the host, before anything could be enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from ring_exact_attention_amd import _bwa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bwa.h")
+
+FAKE = 0x7F0000000000  # an aligned address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bwa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_bwa.LIB_PATH):
+        pytest.skip("libbwa.so not built")
+    return _bwa.lib()
+
+
+def T(B=1, H=2, S=64, D=128, dtype=_bwa.BWA_BF16, ptr=FAKE, strides=None):
+    if strides is None:
+        strides = (H * S * D, S * D, D)
+    return _bwa.Tensor(ptr, dtype, 0, B, H, S, D, *strides)
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(_bwa.EXPORTED) <= set(names)
+    for name in names:
+        assert hasattr(L, name), name
+    assert L.bwa_version() == 1
+
+
+def test_status_strings(L):
+    assert L.bwa_status_string(0) == b"BWA_OK"
+    assert L.bwa_status_string(3) == b"BWA_ERR_WORKSPACE"
+    assert L.bwa_status_string(99) == b"BWA_ERR_UNKNOWN"
+
+
+def ring_fwd(L, q, k, v, o, n=4, sched=0, mode=1, causal=0, scale=0.1, lse=FAKE, ws=None,
+             wsb=0):
+    args = [None if x is None else ctypes.byref(x) for x in (q, k, v)]
+    return L.bwa_ring_fwd(*args, n, sched, mode, causal, scale,
+                          None if o is None else ctypes.byref(o), lse, ws, wsb, None)
+
+
+def expect(L, status, code, fragment):
+    assert status == code, (status, L.bwa_last_error())
+    assert fragment in L.bwa_last_error().decode()
+
+
+def test_ring_fwd_validation(L):
+    q, k, o = T(S=64), T(S=256), T(S=64)
+    E = _bwa
+    expect(L, ring_fwd(L, None, k, k, o), E.BWA_ERR_INVALID_ARG, "q is NULL")
+    expect(L, ring_fwd(L, T(D=96), T(D=96, S=256), T(D=96, S=256), T(D=96)),
+           E.BWA_ERR_UNSUPPORTED, "head dim")
+    expect(L, ring_fwd(L, q, k, k, o, n=0), E.BWA_ERR_INVALID_ARG, "shards")
+    expect(L, ring_fwd(L, q, k, k, o, n=257), E.BWA_ERR_INVALID_ARG, "shards")
+    expect(L, ring_fwd(L, q, k, k, o, causal=1), E.BWA_ERR_UNSUPPORTED, "causal")
+    expect(L, ring_fwd(L, q, k, T(S=256, dtype=0), o), E.BWA_ERR_INVALID_ARG, "dtype")
+    expect(L, ring_fwd(L, q, k, T(S=255), o), E.BWA_ERR_INVALID_ARG, "lengths differ")
+    expect(L, ring_fwd(L, q, k, k, T(S=63)), E.BWA_ERR_INVALID_ARG, "o:")
+    expect(L, ring_fwd(L, T(ptr=FAKE + 2), k, k, o), E.BWA_ERR_UNSUPPORTED, "aligned")
+    expect(L, ring_fwd(L, T(strides=(64 * 2 * 128, 64 * 128, 100)), k, k, o),
+           E.BWA_ERR_UNSUPPORTED, "aligned")
+    expect(L, ring_fwd(L, q, k, k, o, scale=0.0), E.BWA_ERR_INVALID_ARG, "scale")
+    expect(L, ring_fwd(L, q, k, k, o, scale=float("nan")), E.BWA_ERR_INVALID_ARG, "scale")
+    expect(L, ring_fwd(L, q, k, k, o, sched=5), E.BWA_ERR_INVALID_ARG, "schedule")
+    expect(L, ring_fwd(L, q, k, k, o, mode=7), E.BWA_ERR_INVALID_ARG, "mode")
+    expect(L, ring_fwd(L, q, k, k, o, lse=None), E.BWA_ERR_INVALID_ARG, "lse")
+    expect(L, ring_fwd(L, q, T(H=3, S=256), T(H=3, S=256), o), E.BWA_ERR_INVALID_ARG, "head")
+
+
+def test_ring_fwd_workspace_checks(L):
+    q, k, o = T(S=64), T(S=256), T(S=64)
+    need = L.bwa_ring_fwd_workspace(ctypes.byref(q), ctypes.byref(k), 4, _bwa.MODE_ROUNDS)
+    assert need == 2 * 64 * 128 * 4
+    assert L.bwa_ring_fwd_workspace(ctypes.byref(q), ctypes.byref(k), 4, _bwa.MODE_FUSED) == 0
+    split = L.bwa_ring_fwd_workspace(ctypes.byref(q), ctypes.byref(k), 4, _bwa.MODE_SPLIT)
+    assert split == 4 * 2 * 64 * 128 * 4 + 4 * 2 * 64 * 4
+    assert L.bwa_ring_fwd_workspace(ctypes.byref(q), ctypes.byref(k), 0, _bwa.MODE_SPLIT) == 0
+    expect(L, ring_fwd(L, q, k, k, o, mode=_bwa.MODE_ROUNDS, ws=None, wsb=0),
+           _bwa.BWA_ERR_WORKSPACE, "workspace")
+    expect(L, ring_fwd(L, q, k, k, o, mode=_bwa.MODE_SPLIT, ws=FAKE, wsb=split - 1),
+           _bwa.BWA_ERR_WORKSPACE, "workspace")
+    expect(L, ring_fwd(L, q, k, k, o, mode=_bwa.MODE_SPLIT, ws=FAKE + 16, wsb=split),
+           _bwa.BWA_ERR_WORKSPACE, "256-byte")
+
+
+def test_empty_query_is_a_noop(L):
+    q, o = T(S=0, ptr=0), T(S=0, ptr=0)
+    k = T(S=16)
+    assert ring_fwd(L, q, k, k, o, lse=None) == _bwa.BWA_OK
+
+
+def test_partial_fwd_validation(L):
+    q, k = T(S=64), T(S=256)
+    f = L.bwa_partial_fwd
+    E = _bwa
+    expect(L, f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), 0, 65, 0, 16, 0.1, 0, FAKE,
+                FAKE, 0, None), E.BWA_ERR_INVALID_ARG, "query range")
+    expect(L, f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), 0, 64, 250, 16, 0.1, 0, FAKE,
+                FAKE, 0, None), E.BWA_ERR_INVALID_ARG, "key range")
+    expect(L, f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), 0, 64, 0, 16, 0.1, 0, None,
+                FAKE, 0, None), E.BWA_ERR_INVALID_ARG, "NULL")
+    expect(L, f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), 0, 64, 0, 16, 0.1, 0,
+                FAKE + 4, FAKE, 0, None), E.BWA_ERR_UNSUPPORTED, "aligned")
+    assert f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), 5, 0, 0, 16, 0.1, 0, None, None,
+             0, None) == E.BWA_OK
+
+
+def test_merge_validation(L):
+    E = _bwa
+    expect(L, L.bwa_merge(4, 96, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None), E.BWA_ERR_UNSUPPORTED,
+           "D must")
+    expect(L, L.bwa_merge(-1, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None),
+           E.BWA_ERR_INVALID_ARG, "rows")
+    expect(L, L.bwa_merge(4, 64, None, FAKE, FAKE, FAKE, FAKE, FAKE, None), E.BWA_ERR_INVALID_ARG,
+           "NULL")
+    assert L.bwa_merge(0, 64, None, None, None, None, None, None, None) == E.BWA_OK
+
+
+def test_ring_bwd_validation(L):
+    q, k = T(S=64), T(S=256)
+    args = lambda **kw: [ctypes.byref(x) for x in (q, k, k, q)] + [FAKE, ctypes.byref(q), 4, 0,
+                                                                   kw.get("mode", 1), 0, 0.1] + \
+        [ctypes.byref(x) for x in (q, kw.get("dk", k), k)] + [None, 0, None]
+    expect(L, L.bwa_ring_bwd(*args(dk=T(S=255))), _bwa.BWA_ERR_INVALID_ARG, "dk")
+    qf, kf = T(S=64, dtype=0), T(S=256, dtype=0)
+    a = [ctypes.byref(x) for x in (qf, kf, kf, qf)] + [FAKE, ctypes.byref(qf), 4, 0, 1, 0, 0.1] + \
+        [ctypes.byref(x) for x in (qf, kf, kf)] + [None, 0, None]
+    expect(L, L.bwa_ring_bwd(*a), _bwa.BWA_ERR_UNSUPPORTED, "backward")
+
+
+def test_kv_recompute_validation(L):
+    k = T(S=64)
+    E = _bwa
+    f = L.bwa_kv_recompute
+    expect(L, f(FAKE, FAKE, FAKE, 1, 64, 4096, 2, 128, 0, ctypes.byref(k), ctypes.byref(k), None),
+           E.BWA_ERR_UNSUPPORTED, "bf16")
+    expect(L, f(FAKE, FAKE, FAKE, 1, 64, 100, 2, 128, 1, ctypes.byref(k), ctypes.byref(k), None),
+           E.BWA_ERR_UNSUPPORTED, "multiple of 64")
+    expect(L, f(FAKE, FAKE, FAKE, 1, 65, 4096, 2, 128, 1, ctypes.byref(k), ctypes.byref(k), None),
+           E.BWA_ERR_INVALID_ARG, "shape")
+    expect(L, f(None, FAKE, FAKE, 1, 64, 4096, 2, 128, 1, ctypes.byref(k), ctypes.byref(k), None),
+           E.BWA_ERR_INVALID_ARG, "NULL")
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(ValueError, match="GPU memory"):
+        _bwa.bwa_ring_fwd(q, q, q, n=2)
+
+
+def test_product_path_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "ring_exact_attention_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "liboracle" not in text and "oracle.c" not in text, f

@@ -1,0 +1,244 @@
+"""GPU forward parity: HIP path (through the C ABI) vs the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from tests.parity import check_fwd, sample_rows, to64
+
+pytestmark = pytest.mark.gpu
+
+MODES = ["rounds", "fused", "split"]
+SCHEDS = ["kv", "q"]
+
+
+@pytest.fixture(scope="module")
+def bwa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import ring_exact_attention_amd as m
+    m.lib()  # raises if the HIP library is not built
+    return m
+
+
+def gen(B, H, SQ, SKV, D, dtype, seed, std=1.0):
+    g = torch.Generator().manual_seed(seed)
+    q = (torch.randn(B, H, SQ, D, generator=g) * std).to(dtype)
+    k = (torch.randn(B, H, SKV, D, generator=g) * std).to(dtype)
+    v = torch.randn(B, H, SKV, D, generator=g).to(dtype)
+    return q, k, v
+
+
+def log_case(**kw):
+    print("case:", " ".join(f"{a}={b}" for a, b in kw.items()), flush=True)
+
+
+# ------------------------------------------------------------------ tiny fp32 workload
+
+def test_tiny_f32_all_modes(bwa, orc):
+    from ring_exact_attention_amd.inputs import WORKLOADS, make_qkv
+    w = WORKLOADS["tiny_f32"]
+    q, k, v = make_qkv(w)
+    O, L = orc.attn_fwd(q, k, v, w.scale)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    for mode in MODES:
+        for sched in SCHEDS:
+            log_case(test="tiny_f32", mode=mode, sched=sched)
+            o, lse = bwa.bwa_ring_fwd(qd, kd, vd, w.n, sched, mode, scale=w.scale)
+            torch.cuda.synchronize()
+            check_fwd(o, lse, O, L, "f32", f"tiny_f32 {mode}/{sched}")
+
+
+def test_tiny_f32_partials_and_merge(bwa, orc):
+    """The tiny workload as the pages describe one worker's view: four block
+    partials from bwa_partial_fwd merged with bwa_merge, and the same chain
+    with in-kernel accumulation."""
+    from ring_exact_attention_amd.inputs import WORKLOADS, make_qkv
+    w = WORKLOADS["tiny_f32"]
+    q, k, v = make_qkv(w)
+    O, L = orc.attn_fwd(q, k, v, w.scale)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    B, H, SQ, D = q.shape
+    bounds = orc.shard_bounds(w.SKV, w.n)
+    parts = []
+    for a, b in bounds:
+        o = torch.zeros(B, H, SQ, D, device="cuda")
+        l = torch.zeros(B, H, SQ, device="cuda")
+        bwa.bwa_partial_fwd(qd, kd, vd, 0, SQ, a, b - a, w.scale, False, o, l, accumulate=False)
+        parts.append((o, l))
+        Op, Lp = orc.attn_partial(q, k, v, w.scale, False, 0, SQ, a, b)
+        torch.cuda.synchronize()
+        check_fwd(o, l, Op, Lp, "f32", f"partial [{a},{b})")
+    acc_o, acc_l = parts[0][0].clone(), parts[0][1].clone()
+    for o, l in parts[1:]:
+        bwa.bwa_merge(acc_o, acc_l, o, l, acc_o, acc_l)  # in place: outputs alias input a
+    torch.cuda.synchronize()
+    check_fwd(acc_o, acc_l, O, L, "f32", "merge chain")
+    o = torch.zeros(B, H, SQ, D, device="cuda")
+    l = torch.zeros(B, H, SQ, device="cuda")
+    for i, (a, b) in enumerate(reversed(bounds)):
+        bwa.bwa_partial_fwd(qd, kd, vd, 0, SQ, a, b - a, w.scale, False, o, l, accumulate=i > 0)
+    torch.cuda.synchronize()
+    check_fwd(o, l, O, L, "f32", "accumulate chain")
+
+
+# ------------------------------------------------------------------ small bf16 shapes
+
+SHAPES = [
+    # B, H, SQ, SKV, D, n
+    (1, 2, 300, 1000, 128, 4),   # ragged tiles and shards
+    (2, 1, 64, 64, 64, 1),       # one shard, D = 64
+    (1, 1, 1, 7, 128, 7),        # one query, one key per shard
+    (1, 3, 517, 1500, 128, 8),
+    (1, 2, 20, 2048, 128, 16),   # query blocks of one or two rows
+    (1, 1, 5, 100, 128, 8),      # more shards than query rows: empty query blocks
+    (2, 2, 256, 4096, 128, 8),   # full tiles
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_bf16_shapes_all_modes(bwa, orc, shape):
+    B, H, SQ, SKV, D, n = shape
+    q, k, v = gen(B, H, SQ, SKV, D, torch.bfloat16, seed=sum(shape))
+    scale = 1 / math.sqrt(D)
+    O, L = orc.attn_fwd(q, k, v, scale)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    for mode in MODES:
+        for sched in SCHEDS:
+            log_case(shape=shape, mode=mode, sched=sched)
+            o, lse = bwa.bwa_ring_fwd(qd, kd, vd, n, sched, mode, scale=scale)
+            torch.cuda.synchronize()
+            check_fwd(o, lse, O, L, "bf16", f"{shape} {mode}/{sched}")
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 700, 128, 4), (1, 1, 300, 64, 3), (1, 2, 1024, 128, 8),
+                                   (1, 1, 65, 128, 65)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_bf16_causal_all_modes(bwa, orc, shape):
+    B, H, S, D, n = shape
+    q, k, v = gen(B, H, S, S, D, torch.bfloat16, seed=7 + S)
+    scale = 1 / math.sqrt(D)
+    O, L = orc.attn_fwd(q, k, v, scale, causal=True)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    for mode in MODES:
+        for sched in SCHEDS:
+            log_case(causal_shape=shape, mode=mode, sched=sched)
+            o, lse = bwa.bwa_ring_fwd(qd, kd, vd, n, sched, mode, causal=True, scale=scale)
+            torch.cuda.synchronize()
+            check_fwd(o, lse, O, L, "bf16", f"causal {shape} {mode}/{sched}")
+
+
+def test_f32_causal_and_d128(bwa, orc):
+    for (S, D, n, causal) in [(200, 128, 3, True), (96, 64, 5, True), (77, 128, 2, False)]:
+        q, k, v = gen(1, 2, S, S + (0 if causal else 33), D, torch.float32, seed=S)
+        O, L = orc.attn_fwd(q, k, v, 0.1, causal=causal)
+        for mode in MODES:
+            log_case(f32=(S, D, n, causal), mode=mode)
+            o, lse = bwa.bwa_ring_fwd(q.cuda(), k.cuda(), v.cuda(), n, "q", mode, causal=causal,
+                                      scale=0.1)
+            torch.cuda.synchronize()
+            check_fwd(o, lse, O, L, "f32", f"f32 {S} {D} {mode}")
+
+
+def test_partial_fully_masked_rows(bwa, orc):
+    """Causal pair whose keys all lie after some of its rows: those rows get (0, -inf)."""
+    q, k, v = gen(1, 2, 256, 256, 128, torch.bfloat16, seed=3)
+    o = torch.full((1, 2, 256, 128), 7.0, device="cuda")
+    l = torch.full((1, 2, 256), 7.0, device="cuda")
+    bwa.bwa_partial_fwd(q.cuda(), k.cuda(), v.cuda(), 0, 256, 100, 80, 0.125, True, o, l, False)
+    torch.cuda.synchronize()
+    Op, Lp = orc.attn_partial(q, k, v, 0.125, True, 0, 256, 100, 180)
+    check_fwd(o, l, Op, Lp, "bf16", "partial causal")
+    assert torch.all(l[:, :, :100] == -math.inf)
+    assert torch.all(o[:, :, :100] == 0)
+
+
+def test_strided_layouts_and_guard_bands(bwa, orc):
+    """[B, S, H, D] storage viewed as [B, H, S, D]; output written into the
+    middle of a NaN-filled buffer must leave the rest untouched."""
+    B, H, SQ, SKV, D, n = 2, 3, 130, 700, 128, 4
+    q, k, v = gen(B, H, SQ, SKV, D, torch.bfloat16, seed=11)
+    O, L = orc.attn_fwd(q, k, v, 0.09)
+    qs = q.transpose(1, 2).contiguous().cuda().transpose(1, 2)
+    ks = k.transpose(1, 2).contiguous().cuda().transpose(1, 2)
+    vs = v.transpose(1, 2).contiguous().cuda().transpose(1, 2)
+    big = torch.full((B, SQ + 8, H, D + 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    o = big[:, 4:4 + SQ, :, 32:32 + D].transpose(1, 2)
+    for mode in MODES:
+        big.fill_(float("nan"))
+        log_case(strided=mode)
+        _, lse = bwa.bwa_ring_fwd(qs, ks, vs, n, "kv", mode, scale=0.09, o=o)
+        torch.cuda.synchronize()
+        check_fwd(o, lse, O, L, "bf16", f"strided {mode}")
+        mask = torch.ones_like(big, dtype=torch.bool)
+        mask[:, 4:4 + SQ, :, 32:32 + D] = False
+        assert torch.isnan(big[mask].float()).all(), "write outside the output view"
+
+
+def test_hot_rows_peaked_softmax(bwa, orc):
+    """1% of K rows scaled by 8 (peaked softmax): the absolute bound bites here."""
+    from ring_exact_attention_amd.inputs import WORKLOADS, make_qkv
+    w = WORKLOADS["shortq_256_256k"].resized(B=1, H=2, SKV=8192, n=8)
+    q, k, v = make_qkv(w)
+    O, L = orc.attn_fwd(q, k, v, w.scale)
+    for mode in MODES:
+        log_case(hot=mode)
+        o, lse = bwa.bwa_ring_fwd(q.cuda(), k.cuda(), v.cuda(), w.n, "kv", mode, scale=w.scale)
+        torch.cuda.synchronize()
+        check_fwd(o, lse, O, L, "bf16", f"hot rows {mode}")
+
+
+def test_deterministic(bwa):
+    q, k, v = (x.cuda() for x in gen(1, 4, 512, 4096, 128, torch.bfloat16, seed=5))
+    for mode in MODES:
+        a = bwa.bwa_ring_fwd(q, k, v, 8, "kv", mode)
+        b = bwa.bwa_ring_fwd(q, k, v, 8, "kv", mode)
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), mode
+
+
+def test_schedules_agree_closely(bwa):
+    """Both schedules and all modes compute the same pairs: they differ only
+    by fp32 merge rounding."""
+    q, k, v = (x.cuda() for x in gen(1, 2, 512, 8192, 128, torch.bfloat16, seed=9))
+    ref = bwa.bwa_ring_fwd(q, k, v, 8, "kv", "fused")[0].float()
+    for mode in MODES:
+        for sched in SCHEDS:
+            o = bwa.bwa_ring_fwd(q, k, v, 8, sched, mode)[0].float()
+            assert (o - ref).abs().max().item() <= 2 ** -8 * ref.abs().max().item() + 1e-6
+
+
+# ------------------------------------------------------------------ full-size workloads (sampled rows)
+
+def _full_size(bwa, orc, name, modes, scheds, per_head):
+    from ring_exact_attention_amd.inputs import WORKLOADS, make_qkv
+    w = WORKLOADS[name]
+    log_case(workload=name, stage="inputs")
+    q, k, v = make_qkv(w, device="cuda")
+    rows = sample_rows(w.B, w.H, w.SQ, w.n, per_head=per_head, seed=w.seed)
+    log_case(workload=name, stage="oracle", rows=len(rows))
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    O, L = orc.attn_fwd(qc, kc, vc, w.scale, causal=w.causal, rows=rows)
+    del qc, kc, vc
+    for mode in modes:
+        for sched in scheds:
+            log_case(workload=name, mode=mode, sched=sched)
+            o, lse = bwa.bwa_ring_fwd(q, k, v, w.n, sched, mode, causal=w.causal, scale=w.scale)
+            torch.cuda.synchronize()
+            o_s = o.reshape(-1, w.D)[torch.as_tensor(rows, device="cuda")]
+            l_s = lse.reshape(-1)[torch.as_tensor(rows, device="cuda")]
+            check_fwd(o_s, l_s, O, L, w.dtype, f"{name} {mode}/{sched}")
+            assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def test_full_lvx_2k_128k(bwa, orc):
+    _full_size(bwa, orc, "lvx_2k_128k", MODES, SCHEDS, per_head=6)
+
+
+def test_full_shortq_256_256k(bwa, orc):
+    _full_size(bwa, orc, "shortq_256_256k", ["split", "rounds"], SCHEDS, per_head=3)
+
+
+def test_full_causal_64k(bwa, orc):
+    _full_size(bwa, orc, "causal_64k", ["fused", "rounds"], SCHEDS, per_head=4)
