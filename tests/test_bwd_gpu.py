@@ -1,0 +1,147 @@
+"""GPU backward and K/V-recompute parity vs the fp64 oracle (through the C ABI)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from tests.parity import check_grad, to64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bwa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import ring_exact_attention_amd as m
+    m.lib()
+    return m
+
+
+def log_case(**kw):
+    print("case:", " ".join(f"{a}={b}" for a, b in kw.items()), flush=True)
+
+
+def gen(B, H, SQ, SKV, D, seed, std=0.5):
+    g = torch.Generator().manual_seed(seed)
+    q = (torch.randn(B, H, SQ, D, generator=g) * std).bfloat16()
+    k = (torch.randn(B, H, SKV, D, generator=g) * std).bfloat16()
+    v = (torch.randn(B, H, SKV, D, generator=g) * std).bfloat16()
+    do = torch.randn(B, H, SQ, D, generator=g).bfloat16()
+    return q, k, v, do
+
+
+BWD_SHAPES = [
+    # B, H, SQ, SKV, n, causal
+    (1, 2, 256, 1024, 4, False),
+    (1, 2, 300, 1000, 4, False),   # ragged tiles and shards
+    (2, 1, 65, 130, 3, False),
+    (1, 1, 5, 100, 8, False),      # empty query blocks
+    (1, 2, 512, 512, 4, True),
+    (1, 1, 300, 300, 3, True),
+]
+
+
+@pytest.mark.parametrize("shape", BWD_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_bwd_small(bwa, orc, shape):
+    B, H, SQ, SKV, n, causal = shape
+    D = 128
+    scale = 1 / math.sqrt(D)
+    q, k, v, do = gen(B, H, SQ, SKV, D, seed=SQ + SKV)
+    ref = orc.attn_bwd(q, k, v, do, scale, causal)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = bwa.bwa_ring_fwd(qd, kd, vd, n, "kv", "fused", causal=causal, scale=scale)
+    for mode in ("fused", "rounds"):
+        for sched in ("kv", "q"):
+            log_case(shape=shape, mode=mode, sched=sched)
+            dq, dk, dv = bwa.bwa_ring_bwd(qd, kd, vd, o, lse, dod, n, sched, mode, causal=causal,
+                                          scale=scale)
+            torch.cuda.synchronize()
+            check_grad(dq.reshape(B * H, SQ, D), ref["dq"], f"dq {shape} {mode}/{sched}")
+            check_grad(dk.reshape(B * H, SKV, D), ref["dk"], f"dk {shape} {mode}/{sched}")
+            check_grad(dv.reshape(B * H, SKV, D), ref["dv"], f"dv {shape} {mode}/{sched}")
+
+
+def test_bwd_deterministic(bwa):
+    q, k, v, do = (x.cuda() for x in gen(1, 2, 512, 4096, 128, seed=1))
+    o, lse = bwa.bwa_ring_fwd(q, k, v, 8)
+    for mode in ("fused", "rounds"):
+        a = bwa.bwa_ring_bwd(q, k, v, o, lse, do, 8, "kv", mode)
+        b = bwa.bwa_ring_bwd(q, k, v, o, lse, do, 8, "kv", mode)
+        torch.cuda.synchronize()
+        for x, y in zip(a, b):
+            assert torch.equal(x, y), mode
+
+
+def test_kv_recompute_small(bwa, orc):
+    for (B, S, E, H, D) in [(2, 300, 128, 2, 128), (1, 1000, 256, 3, 128), (1, 64, 64, 2, 64)]:
+        g = torch.Generator().manual_seed(S)
+        y = (torch.randn(B, S, E, generator=g) * 0.5).bfloat16()
+        wk = (torch.randn(H * D, E, generator=g) * 0.1).bfloat16()
+        wv = (torch.randn(H * D, E, generator=g) * 0.1).bfloat16()
+        log_case(recompute=(B, S, E, H, D))
+        k, v = bwa.bwa_kv_recompute(y.cuda(), wk.cuda(), wv.cuda(), H, D)
+        torch.cuda.synchronize()
+        for got, w in ((k, wk), (v, wv)):
+            ref = orc.kv_proj(y, w, H, D)
+            err = np.abs(to64(got) - ref)
+            # one bf16 rounding of the fp32 accumulator: half an ulp, <= 2^-8 relative
+            assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-6), err.max()
+
+
+def test_kv_recompute_strided_output(bwa, orc):
+    """Write K into a [B, S, H, D] buffer through strides."""
+    B, S, E, H, D = 1, 200, 128, 2, 128
+    g = torch.Generator().manual_seed(4)
+    y = (torch.randn(B, S, E, generator=g) * 0.5).bfloat16()
+    w = (torch.randn(H * D, E, generator=g) * 0.1).bfloat16()
+    kb = torch.zeros(B, S, H, D, dtype=torch.bfloat16, device="cuda")
+    vb = torch.zeros(B, H, S, D, dtype=torch.bfloat16, device="cuda")
+    bwa.bwa_kv_recompute(y.cuda(), w.cuda(), w.cuda(), H, D, k=kb.transpose(1, 2), v=vb)
+    torch.cuda.synchronize()
+    ref = orc.kv_proj(y, w, H, D)
+    assert np.abs(to64(kb.transpose(1, 2)) - ref).max() <= 2.0 ** -8 * np.abs(ref).max()
+    assert torch.equal(kb.transpose(1, 2), vb)
+
+
+def test_full_recompute_bwd(bwa, orc):
+    """Recompute + backward workload: y [1, 65536, 4096], W_k, W_v [4096, 4096],
+    32 heads, S_Q = 2048, n = 8.  Checks sampled K/V rows of the GEMM against the
+    exact fp64 projection, and dQ/dK/dV of two full heads against the oracle's
+    exact gradients computed from the exact (fp64) K and V."""
+    from ring_exact_attention_amd.inputs import WORKLOADS, make_dout, make_qkv, make_recompute
+    w = WORKLOADS["recompute_bwd"]
+    log_case(workload=w.name, stage="inputs")
+    y, wk, wv = make_recompute(w, device="cuda")
+    q, _, _ = make_qkv(w.resized(SKV=1), device="cuda")
+    do = make_dout(w, device="cuda")
+    k, v = bwa.bwa_kv_recompute(y, wk, wv, w.H, w.D)
+    o, lse = bwa.bwa_ring_fwd(q, k, v, w.n, "kv", "fused", scale=w.scale)
+    dq, dk, dv = bwa.bwa_ring_bwd(q, k, v, o, lse, do, w.n, "kv", "fused", scale=w.scale)
+    torch.cuda.synchronize()
+    for x in (k, v, o, dq, dk, dv):
+        assert torch.isfinite(x).all()
+
+    yc, wkc, wvc = y.cpu(), wk.cpu(), wv.cpu()
+    g = np.random.default_rng(w.seed)
+    rows = np.sort(g.choice(w.SKV, size=64, replace=False))
+    log_case(workload=w.name, stage="oracle projection rows")
+    for got, wt in ((k, wkc), (v, wvc)):
+        ref = orc.kv_proj(yc, wt, w.H, w.D, rows=rows).reshape(len(rows), w.H, w.D)
+        gs = to64(got[0, :, torch.as_tensor(rows, device="cuda")].permute(1, 0, 2))
+        assert np.all(np.abs(gs - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6)
+
+    heads = [0, 17]
+    log_case(workload=w.name, stage="oracle exact K, V of two heads")
+    K = np.stack([orc.kv_proj(yc, wkc[h * w.D:(h + 1) * w.D], 1, w.D)[0, 0] for h in heads])[None]
+    V = np.stack([orc.kv_proj(yc, wvc[h * w.D:(h + 1) * w.D], 1, w.D)[0, 0] for h in heads])[None]
+    qh = q[:, heads].cpu().double().numpy()
+    doh = do[:, heads].cpu().double().numpy()
+    keys = np.sort(g.choice(w.SKV, size=256, replace=False))
+    log_case(workload=w.name, stage="oracle backward")
+    ref = orc.attn_bwd(qh, K, V, doh, w.scale, keys=keys)
+    kk = torch.as_tensor(keys, device="cuda")
+    check_grad(dq[0, heads], ref["dq"], "dq full")
+    check_grad(dk[0, heads][:, kk], ref["dk"], "dk full (sampled keys)")
+    check_grad(dv[0, heads][:, kk], ref["dv"], "dv full (sampled keys)")
