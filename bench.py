@@ -87,6 +87,9 @@ def main():
     ap.add_argument("--sched", default="kv", choices=["kv", "q"])
     ap.add_argument("--cpu-rows-per-head", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, copy one 1 GiB buffer (a plain copy kernel of "
+                         "known size, to calibrate HBM byte counters taken under a profiler)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -174,6 +177,13 @@ def main():
                    "causal": w.causal, "seed": w.seed},
         "roofline": roofline,
     }
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(q, k, v, w, args.cpu_rows_per_head)
     else:

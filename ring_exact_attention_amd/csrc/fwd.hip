@@ -14,8 +14,15 @@
 // exchange with lane l^32.  The PV product is O^T = V^T P^T, whose B operand
 // is exactly the lane's own scores converted to bf16, and whose accumulator
 // rows are rescaled by the lane's own factor.  V^T needs keys contiguous in
-// the A operand, so V tiles are stored in LDS as [key/4][d][4] (four keys of
-// one column in 8 bytes), transposed in registers while staging.
+// the A operand: V tiles are staged row-major like K, and the operand is read
+// with ds_read_b64_tr_b16, which hands each lane one column of a 4-row block
+// (four keys of one head dim).
+//
+// The running maximum is only moved when some row's maximum grows by more
+// than 2^8 (log2 units): until then probabilities are taken relative to the
+// stale maximum (they stay <= 256, exact in fp32 and bf16 range), and the
+// O accumulator is not rescaled.  Output and LSE are unchanged by this: O and
+// l always share one reference maximum.
 //
 // fp32 kernel: plain VALU arithmetic (fp32 products and sums), four lanes per
 // query row; used for fp32 inputs where fp32-exact products are required.
@@ -39,6 +46,12 @@ __device__ inline float wave_swap32_sum(float x) {
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Growth of a row maximum (log2 units) tolerated before the O accumulator is rescaled.
+constexpr float kLazyRescale = 8.f;
 
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
   bf16 x = (bf16)a, y = (bf16)b;  // round to nearest even (v_cvt_pk_bf16_f32)
@@ -65,24 +78,24 @@ struct Bf16Fwd {
   static constexpr int BM = 32 * NW;           // query rows per workgroup
   static constexpr int NT = 64 * NW;           // threads
   static constexpr int KS = D + 8;             // K row stride in LDS (elements), 16 B pad
+  static constexpr int VS = D + 16;            // V row stride (elements), 32 B pad: the four
+                                               // rows of a transposing read hit disjoint banks
   static constexpr int K_TILE = BN * KS;       // elements
-  static constexpr int V_TILE = BN * D;        // elements, [BN/4][D][4]
+  static constexpr int V_TILE = BN * VS;       // elements, row-major
   static constexpr int HALF = NT / 2;          // threads staging K (first half) / V (second)
-  static constexpr int KC = (BN * D / 8) / HALF;   // 16-byte K chunks per staging thread
-  static constexpr int VI = (BN * D / 32) / HALF;  // 4-row V items per staging thread
+  static constexpr int KC = (BN * D / 8) / HALF;   // 16-byte chunks per staging thread
   static constexpr int NLD = KC;                    // 16-byte loads in flight per thread
-  static_assert(KC * HALF == BN * D / 8, "K staging must divide evenly");
-  static_assert(VI * HALF == BN * D / 32 && VI * 4 == KC, "V staging must match K staging");
+  static_assert(KC * HALF == BN * D / 8, "staging must divide evenly");
   static constexpr int LDS_BYTES = (2 * K_TILE + 2 * V_TILE) * 2;
 };
 
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdParams p) {
   using C = Bf16Fwd<D, NW>;
-  constexpr int BN = C::BN, KS = C::KS, HALF = C::HALF;
+  constexpr int BN = C::BN, KS = C::KS, VS = C::VS, HALF = C::HALF;
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::K_TILE + 2 * C::V_TILE];
   bf16* Ks = smem;                     // [2][BN][KS]
-  bf16* Vs = smem + 2 * C::K_TILE;     // [2][BN/4][D][4]
+  bf16* Vs = smem + 2 * C::K_TILE;     // [2][BN][KS]
 
   Job jb;
   if (!make_job(p, C::BM, &jb)) return;
@@ -141,54 +154,26 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdParams p) {
   // ---- staging: global -> registers -> LDS
   u32x4 stg[C::NLD];
   auto load_tile = [&](int64_t kt, int64_t ke) {
-    if (tid < HALF) {
+    const bf16* src = tid < HALF ? kg : vg;
+    const int64_t ss = tid < HALF ? p.skS : p.svS;
+    const int t2 = tid < HALF ? tid : tid - HALF;
 #pragma unroll
-      for (int i = 0; i < C::KC; ++i) {
-        int c = tid + i * HALF;
-        int row = c / (D / 8), col8 = c % (D / 8);
-        int64_t key = kt + row;
-        stg[i] = key < ke ? *(const u32x4*)(kg + key * p.skS + col8 * 8) : u32x4{};
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < C::VI; ++i) {
-        int itm = (tid - HALF) + i * HALF;
-        int quad = itm / (D / 8), col8 = itm % (D / 8);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          int64_t key = kt + 4 * quad + rr;
-          stg[4 * i + rr] = key < ke ? *(const u32x4*)(vg + key * p.svS + col8 * 8) : u32x4{};
-        }
-      }
+    for (int i = 0; i < C::KC; ++i) {
+      int c = t2 + i * HALF;
+      int row = c / (D / 8), col8 = c % (D / 8);
+      int64_t key = kt + row;
+      stg[i] = key < ke ? *(const u32x4*)(src + key * ss + col8 * 8) : u32x4{};
     }
   };
   auto store_tile = [&](int buf) {
-    if (tid < HALF) {
-      bf16* kd = Ks + buf * C::K_TILE;
+    bf16* dst = (tid < HALF ? Ks + buf * C::K_TILE : Vs + buf * C::V_TILE);
+    const int t2 = tid < HALF ? tid : tid - HALF;
+    const int rs = tid < HALF ? KS : VS;
 #pragma unroll
-      for (int i = 0; i < C::KC; ++i) {
-        int c = tid + i * HALF;
-        int row = c / (D / 8), col8 = c % (D / 8);
-        *(u32x4*)(kd + row * KS + col8 * 8) = stg[i];
-      }
-    } else {
-      bf16* vd = Vs + buf * C::V_TILE;
-#pragma unroll
-      for (int i = 0; i < C::VI; ++i) {
-        int itm = (tid - HALF) + i * HALF;
-        int quad = itm / (D / 8), col8 = itm % (D / 8);
-        const u32x4 r0 = stg[4 * i], r1 = stg[4 * i + 1], r2 = stg[4 * i + 2], r3 = stg[4 * i + 3];
-        bf16* dst = vd + (quad * D + col8 * 8) * 4;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          // columns 2w (low halves) and 2w+1 (high halves) of the four rows
-          uint32_t lo01 = (r0[w] & 0xffffu) | (r1[w] << 16);
-          uint32_t lo23 = (r2[w] & 0xffffu) | (r3[w] << 16);
-          uint32_t hi01 = (r0[w] >> 16) | (r1[w] & 0xffff0000u);
-          uint32_t hi23 = (r2[w] >> 16) | (r3[w] & 0xffff0000u);
-          *(u32x4*)(dst + 8 * w) = u32x4{lo01, lo23, hi01, hi23};
-        }
-      }
+    for (int i = 0; i < C::KC; ++i) {
+      int c = t2 + i * HALF;
+      int row = c / (D / 8), col8 = c % (D / 8);
+      *(u32x4*)(dst + row * rs + col8 * 8) = stg[i];
     }
   };
 
@@ -244,12 +229,20 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[u][e]);
     mx = wave_swap32_max(mx);
-    const float m_new = fmaxf(m2, mx * c2);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m2 - m_use);
-    m2 = m_new;
+    const float m_cand = fmaxf(m2, mx * c2);
+    if (__builtin_amdgcn_ballot_w64(m_cand > m2 + kLazyRescale) != 0) {
+      // some row's maximum grew by more than 2^8: move every row to its new maximum
+      const float alpha = fast_exp2(m2 - ((m_cand == -INFINITY) ? 0.f : m_cand));
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+      m2 = m_cand;
+    }
+    const float m_use = (m2 == -INFINITY) ? 0.f : m2;
 
-    float tsum = 0.f;
+    float ts[4] = {0.f, 0.f, 0.f, 0.f};
     bf16x8 pb[BN / 16];
 #pragma unroll
     for (int u = 0; u < BN / 32; ++u)
@@ -259,28 +252,28 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           pv[e] = fast_exp2(__builtin_fmaf(sacc[u][8 * hh + e], c2, -m_use));
-          tsum += pv[e];
+          ts[e & 3] += pv[e];
         }
         bf16x8 x;
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = (bf16)pv[e];
         pb[2 * u + hh] = x;
       }
-    lsum = lsum * alpha + tsum;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+    lsum += (ts[0] + ts[1]) + (ts[2] + ts[3]);
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T.  A operand rows d = 32*dt + lane%32, keys 16t + 4g + {0..3}
+    // and 16t + 8 + 4g + {0..3}: two transposing reads of 4-row blocks.
+    const int li = lane & 15;
+    const bf16* vbase = vt_s + (li >> 2) * VS + ((lane >> 4) & 1) * 16 + 4 * (li & 3);
 #pragma unroll
     for (int t = 0; t < BN / 16; ++t) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const int d = 32 * dt + lr;
-        u32x2 lo = *(const u32x2*)(vt_s + ((4 * t + g) * D + d) * 4);
-        u32x2 hi = *(const u32x2*)(vt_s + ((4 * t + 2 + g) * D + d) * 4);
-        u32x4 av = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        const bf16* a0 = vbase + (16 * t + 4 * g) * VS + 32 * dt;
+        s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
+        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0 + 8 * VS));
+        u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        u32x4 av = u32x4{l2[0], l2[1], h2[0], h2[1]};
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb[t],
                                                            oacc[dt], 0, 0, 0);
       }
