@@ -83,7 +83,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="lvx_2k_128k")
-    ap.add_argument("--mode", default="fused", choices=["rounds", "fused", "split"])
+    ap.add_argument("--mode", default="split", choices=["rounds", "fused", "split"])
     ap.add_argument("--sched", default="kv", choices=["kv", "q"])
     ap.add_argument("--cpu-rows-per-head", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -111,15 +111,41 @@ def main():
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    q, k, v = make_qkv(w, device=dev)
+    recompute = w.E > 0
+    if recompute:
+        from ring_exact_attention_amd.inputs import make_dout, make_recompute
+        y, wk, wv = make_recompute(w, device=dev)
+        q, _, _ = make_qkv(w.resized(SKV=1), device=dev)
+        do = make_dout(w, device=dev)
+        k = torch.empty(w.B, w.H, w.SKV, w.D, dtype=q.dtype, device=dev)
+        v = torch.empty_like(k)
+        bwa.bwa_kv_recompute(y, wk, wv, w.H, w.D, k=k, v=v)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        bmode = "rounds" if args.mode == "rounds" else "fused"
+        bws = torch.empty(max(bwa.ring_bwd_workspace(q, k, w.n, bmode), 1), dtype=torch.uint8,
+                          device=dev)
+    else:
+        q, k, v = make_qkv(w, device=dev)
     o = torch.empty_like(q)
     lse = torch.empty(w.B, w.H, w.SQ, dtype=torch.float32, device=dev)
     nbytes = bwa.ring_fwd_workspace(q, k, w.n, args.mode)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
 
-    def step():
+    def fwd():
         bwa.bwa_ring_fwd(q, k, v, w.n, args.sched, args.mode, causal=w.causal, scale=w.scale,
                          o=o, lse=lse, workspace=ws)
+
+    def step():
+        if recompute:
+            # training step of one cross-attention layer with activation recompute:
+            # K, V from the shared y, forward, K, V recomputed, backward
+            bwa.bwa_kv_recompute(y, wk, wv, w.H, w.D, k=k, v=v)
+            fwd()
+            bwa.bwa_kv_recompute(y, wk, wv, w.H, w.D, k=k, v=v)
+            bwa.bwa_ring_bwd(q, k, v, o, lse, do, w.n, args.sched, bmode, causal=w.causal,
+                             scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=bws)
+        else:
+            fwd()
 
     for _ in range(args.warmup):
         step()
@@ -141,22 +167,55 @@ def main():
         flops = 4.0 * w.B * w.H * w.D * w.SQ * (w.SQ + 1) / 2
     else:
         flops = 4.0 * w.B * w.H * w.SQ * w.SKV * w.D
+    if recompute:
+        gemm = 2.0 * w.B * w.SKV * w.E * w.H * w.D   # one projection
+        flops = flops + 4 * gemm + 2.5 * flops      # fwd + 2x(K, V) recompute + bwd (10 S_Q S_KV D)
     tflops = flops / (ms * 1e-3) / 1e12
+    # compulsory HBM bytes of the forward: read Q, K, V once, write O and LSE
+    esz = 2 if w.dtype == "bf16" else 4
+    fwd_bytes = (w.B * w.H * (2 * w.SQ + 2 * w.SKV) * w.D * esz + w.B * w.H * w.SQ * 4)
 
     # Dominant kernel: in fused mode the step is one launch of the block-pair
     # kernel; in rounds mode n launches (one per round) plus a small finalize;
     # in split mode one launch plus the merge.  Per-launch flops are the
     # step's flops divided by the launches of that kernel.
     launches = w.n if args.mode == "rounds" else 1
-    achieved = (flops / launches) / ((ms * 1e-3) / launches) / 1e12
-    traffic = read_traffic(args.mode)
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic, "kernel": "fwd_bf16_kernel<128,8>",
-                "launches_per_step": launches}
+    if recompute:
+        # several kernels per step (GEMM, forward, backward); report the step as a whole
+        roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                    "traffic": None, "kernel": "whole step (gemm_kv, fwd, bwd kernels)",
+                    "launches_per_step": None}
+    else:
+        # the forward kernel's share of the step: in split mode the merge kernel is
+        # the rest; its duration is measured separately below
+        fwd_ms = ms
+        if args.mode == "split":
+            # the step is two launches: every pair's partial, then the ordered
+            # merge; time the merge alone on the same workspace and subtract
+            from ring_exact_attention_amd._bwa import split_workspace_views
+            op, lp = split_workspace_views(ws, w.n, w.B, w.H, w.SQ, w.D)
+            em = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            bwa.bwa_merge_partials(op, lp, w.n, args.sched, o=o, lse=lse)
+            em[0].record(stream)
+            for _ in range(args.steps):
+                bwa.bwa_merge_partials(op, lp, w.n, args.sched, o=o, lse=lse)
+            em[1].record(stream)
+            torch.cuda.synchronize()
+            merge = em[0].elapsed_time(em[1]) / args.steps
+            fwd_ms = max(ms - merge, 1e-6)
+        achieved = (flops / launches) / ((fwd_ms * 1e-3) / launches) / 1e12
+        traffic = read_traffic(args.mode) if args.workload == "lvx_2k_128k" else None
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": traffic, "kernel": "fwd_bf16_kernel<128,8,64>",
+                    "launches_per_step": launches,
+                    "kernel_ms_per_launch": round(fwd_ms / launches, 4),
+                    "other_ms_per_step": round(ms - fwd_ms, 4)}
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == "lvx_2k_128k" else
+        f"{'training-step' if recompute else 'attention'} TFLOP/s, {w.name}, 1 GPU",
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -177,6 +236,9 @@ def main():
                    "causal": w.causal, "seed": w.seed},
         "roofline": roofline,
     }
+    if not recompute:
+        out["hbm_GBps_compulsory"] = round(fwd_bytes / (ms * 1e-3) / 1e9, 1)
+        out["hbm_frac_compulsory"] = round(fwd_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -184,7 +246,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not recompute:
         out["cpu_baseline"] = cpu_baseline(q, k, v, w, args.cpu_rows_per_head)
     else:
         out["cpu_baseline"] = None

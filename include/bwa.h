@@ -130,6 +130,24 @@ bwa_status bwa_merge(int64_t rows, int64_t D, const float* o_a, const float* lse
                      const float* o_b, const float* lse_b, float* o_out, float* lse_out,
                      void* stream);
 
+/*
+ * n-way merge of per-shard partials in each query block's ring order (the
+ * running (O, L) of the LV-XAttn review's "What carries the argument",
+ * combined shard by shard): for a row of query block j the partials of KV
+ * shards j, j+1, ... (KV-stationary) or j, j-1, ... (Q-stationary), mod n,
+ * are rescale-merged into the identity (0, -inf) in that order.
+ *   o_parts   fp32 [n][B, H, S_Q, D] contiguous, partial k from KV shard k.
+ *   lse_parts fp32 [n][B, H, S_Q] contiguous.
+ *   o         [B, H, S_Q, D] output tensor (fp32 or bf16, any strides).
+ *   lse       fp32 [B, H, S_Q] output.
+ * Query blocks use the n-way split of S_Q (conventions above).  This is the
+ * second launch of bwa_ring_fwd's SPLIT mode, whose workspace holds o_parts
+ * then lse_parts (each region 256-byte aligned).
+ */
+bwa_status bwa_merge_partials(int n, bwa_schedule sched, const float* o_parts,
+                              const float* lse_parts, const bwa_tensor* o, float* lse,
+                              void* stream);
+
 /* Bytes of workspace bwa_ring_fwd needs (0 if none); 0 also for invalid arguments. */
 size_t bwa_ring_fwd_workspace(const bwa_tensor* q, const bwa_tensor* k, int n, bwa_mode mode);
 

@@ -13,6 +13,7 @@ from ._bwa import (  # noqa: F401
     SCHED_Q_STATIONARY,
     bwa_kv_recompute,
     bwa_merge,
+    bwa_merge_partials,
     bwa_partial_fwd,
     bwa_ring_bwd,
     bwa_ring_fwd,
@@ -21,5 +22,6 @@ from ._bwa import (  # noqa: F401
     ring_fwd_workspace,
 )
 
-__all__ = ["bwa_partial_fwd", "bwa_merge", "bwa_ring_fwd", "bwa_ring_bwd", "bwa_kv_recompute",
+__all__ = ["bwa_partial_fwd", "bwa_merge", "bwa_merge_partials", "bwa_ring_fwd", "bwa_ring_bwd",
+           "bwa_kv_recompute",
            "BwaError", "lib"]

@@ -26,7 +26,8 @@ SCHEDULES = {"kv": SCHED_KV_STATIONARY, "lv": SCHED_KV_STATIONARY, "kv_stationar
              "q": SCHED_Q_STATIONARY, "ring": SCHED_Q_STATIONARY, "q_stationary": 1}
 MODES = {"rounds": MODE_ROUNDS, "fused": MODE_FUSED, "split": MODE_SPLIT}
 
-EXPORTED = ("bwa_partial_fwd", "bwa_merge", "bwa_ring_fwd_workspace", "bwa_ring_fwd",
+EXPORTED = ("bwa_partial_fwd", "bwa_merge", "bwa_merge_partials", "bwa_ring_fwd_workspace",
+            "bwa_ring_fwd",
             "bwa_ring_bwd_workspace", "bwa_ring_bwd", "bwa_kv_recompute", "bwa_status_string",
             "bwa_last_error", "bwa_version")
 
@@ -60,6 +61,7 @@ def lib():
         T = ctypes.POINTER(Tensor)
         L.bwa_partial_fwd.argtypes = [T, T, T, i64, i64, i64, i64, f32, ci, vp, vp, ci, vp]
         L.bwa_merge.argtypes = [i64, i64, vp, vp, vp, vp, vp, vp, vp]
+        L.bwa_merge_partials.argtypes = [ci, ci, vp, vp, T, vp, vp]
         L.bwa_ring_fwd_workspace.argtypes = [T, T, ci, ci]
         L.bwa_ring_fwd_workspace.restype = sz
         L.bwa_ring_fwd.argtypes = [T, T, T, ci, ci, ci, ci, f32, T, vp, vp, sz, vp]
@@ -68,8 +70,8 @@ def lib():
         L.bwa_ring_bwd.argtypes = [T, T, T, T, vp, T, ci, ci, ci, ci, f32, T, T, T, vp, sz, vp]
         L.bwa_kv_recompute.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int32, T, T,
                                        vp]
-        for name in ("bwa_partial_fwd", "bwa_merge", "bwa_ring_fwd", "bwa_ring_bwd",
-                     "bwa_kv_recompute"):
+        for name in ("bwa_partial_fwd", "bwa_merge", "bwa_merge_partials", "bwa_ring_fwd",
+                     "bwa_ring_bwd", "bwa_kv_recompute"):
             getattr(L, name).restype = ci
         L.bwa_status_string.argtypes = [ci]
         L.bwa_status_string.restype = ctypes.c_char_p
@@ -148,6 +150,31 @@ def bwa_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None):
     _check(lib().bwa_merge(rows, D, _ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o_out),
                            _ptr(lse_out), _stream(o_a.device)))
     return o_out, lse_out
+
+
+def bwa_merge_partials(o_parts, lse_parts, n, sched="kv", o=None, lse=None, dtype=None):
+    """Merge n per-shard partials (o_parts fp32 [n,B,H,S_Q,D], lse_parts fp32
+    [n,B,H,S_Q]) in each query block's ring order; returns (o, lse)."""
+    for t in (o_parts, lse_parts):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("partials must be contiguous float32")
+    _, B, H, SQ, D = o_parts.shape
+    if o is None:
+        o = torch.empty(B, H, SQ, D, dtype=dtype or torch.float32, device=o_parts.device)
+    if lse is None:
+        lse = torch.empty(B, H, SQ, dtype=torch.float32, device=o_parts.device)
+    to = as_bwa(o)
+    _check(lib().bwa_merge_partials(int(n), _sched(sched), _ptr(o_parts), _ptr(lse_parts),
+                                    ctypes.byref(to), _ptr(lse), _stream(o_parts.device)))
+    return o, lse
+
+
+def split_workspace_views(workspace, n, B, H, SQ, D):
+    """(o_parts, lse_parts) views of a SPLIT-mode forward workspace."""
+    a = (n * B * H * SQ * D * 4 + 255) // 256 * 256
+    o_parts = workspace[: n * B * H * SQ * D * 4].view(torch.float32).view(n, B, H, SQ, D)
+    lse_parts = workspace[a: a + n * B * H * SQ * 4].view(torch.float32).view(n, B, H, SQ)
+    return o_parts, lse_parts
 
 
 def _sched(s) -> int:

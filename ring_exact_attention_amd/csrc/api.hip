@@ -218,6 +218,34 @@ bwa_status bwa_merge(int64_t rows, int64_t D, const float* o_a, const float* lse
   return BWA_OK;
 }
 
+bwa_status bwa_merge_partials(int n, bwa_schedule sched, const float* o_parts,
+                              const float* lse_parts, const bwa_tensor* o, float* lse,
+                              void* stream) {
+  bwa_status s;
+  if ((s = check_tensor(o, "o", true)) != BWA_OK) return s;
+  if ((s = check_sched(sched)) != BWA_OK) return s;
+  if (n < 1 || n > 4096) return fail(BWA_ERR_INVALID_ARG, "n = %d outside [1, 4096]", n);
+  if (o->S == 0) return BWA_OK;
+  if (!o_parts || !lse_parts || !lse) return fail(BWA_ERR_INVALID_ARG, "NULL pointer argument");
+  if ((uintptr_t)o_parts % 16 != 0)
+    return fail(BWA_ERR_UNSUPPORTED, "o_parts must be 16-byte aligned");
+  bwa::FwdParams p = {};
+  p.B = (int)o->B;
+  p.H = (int)o->H;
+  p.SQ = (int)o->S;
+  p.D = (int)o->D;
+  p.n = n;
+  p.sched = sched;
+  p.o = o->ptr;
+  p.soB = o->sB; p.soH = o->sH; p.soS = o->sS;
+  p.lse = lse;
+  p.o_acc = (float*)o_parts;
+  p.lse_part = (float*)lse_parts;
+  hipError_t e = bwa::split_merge_launch(p, o->dtype == BWA_BF16, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "merge partials launch");
+  return BWA_OK;
+}
+
 size_t bwa_ring_fwd_workspace(const bwa_tensor* q, const bwa_tensor* k, int n, bwa_mode mode) {
   if (!q || !k || q->B <= 0 || q->H <= 0 || q->S < 0 || (q->D != 64 && q->D != 128) || n < 1)
     return 0;

@@ -125,6 +125,11 @@ def test_partial_fwd_validation(L):
 
 def test_merge_validation(L):
     E = _bwa
+    o = T(S=8)
+    expect(L, L.bwa_merge_partials(0, 0, FAKE, FAKE, ctypes.byref(o), FAKE, None),
+           E.BWA_ERR_INVALID_ARG, "n = 0")
+    expect(L, L.bwa_merge_partials(2, 3, FAKE, FAKE, ctypes.byref(o), FAKE, None),
+           E.BWA_ERR_INVALID_ARG, "schedule")
     expect(L, L.bwa_merge(4, 96, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None), E.BWA_ERR_UNSUPPORTED,
            "D must")
     expect(L, L.bwa_merge(-1, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None),

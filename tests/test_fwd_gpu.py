@@ -243,3 +243,29 @@ def test_full_shortq_256_256k(bwa, orc):
 
 def test_full_causal_64k(bwa, orc):
     _full_size(bwa, orc, "causal_64k", ["fused", "rounds"], SCHEDS, per_head=4)
+
+
+@pytest.mark.parametrize("sched", SCHEDS)
+def test_merge_partials_vs_oracle(bwa, orc, sched):
+    """Oracle partials of each KV shard, merged on the GPU in every query
+    block's ring order, equal unblocked attention."""
+    B, H, SQ, SKV, D, n = 1, 2, 37, 300, 128, 5
+    q, k, v = gen(B, H, SQ, SKV, D, torch.float32, seed=21)
+    O, L = orc.attn_fwd(q, k, v, 0.1)
+    parts = [orc.attn_partial(q, k, v, 0.1, False, 0, SQ, a, b) for a, b in orc.shard_bounds(SKV, n)]
+    op = torch.tensor(np.stack([p[0] for p in parts]), dtype=torch.float32, device="cuda")
+    lp = torch.tensor(np.stack([p[1] for p in parts]), dtype=torch.float32, device="cuda")
+    o, lse = bwa.bwa_merge_partials(op, lp, n, sched)
+    torch.cuda.synchronize()
+    check_fwd(o, lse, O, L, "f32", f"merge_partials {sched}")
+
+
+def test_split_workspace_merge_matches_ring(bwa):
+    q, k, v = (x.cuda() for x in gen(1, 2, 300, 2000, 128, torch.bfloat16, seed=22))
+    from ring_exact_attention_amd._bwa import split_workspace_views
+    ws = torch.empty(bwa.ring_fwd_workspace(q, k, 4, "split"), dtype=torch.uint8, device="cuda")
+    o, lse = bwa.bwa_ring_fwd(q, k, v, 4, "q", "split", workspace=ws)
+    op, lp = split_workspace_views(ws, 4, 1, 2, 300, 128)
+    o2, lse2 = bwa.bwa_merge_partials(op, lp, 4, "q", dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
