@@ -77,6 +77,78 @@ def cpu_baseline(q, k, v, w, rows_per_head: int):
                       f"all {w.B * w.H} heads) against all {w.SKV} keys, fp64, {dt:.1f} s"}
 
 
+def _find(d: str, suffix: str) -> str:
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def summarize_traffic(fetch_dir: str, write_dir: str, mode: str, command: str) -> str:
+    """Write the committed HBM-traffic summary from two rocprofv3 counter passes
+    (FETCH_SIZE, then WRITE_SIZE) of `bench.py --copy-calibration`.  Each counter
+    is scaled by what it reads for the 1 GiB copy kernel of the same run."""
+    import collections
+    import csv
+
+    def read(d, counter):
+        per = collections.defaultdict(list)
+        for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
+            if r["Counter_Name"] == counter:
+                per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return per
+
+    fe, wr = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
+    ck = next(k for k in fe if "copyBuffer" in k)
+    kk = next(k for k in fe if "fwd_bf16_kernel" in k)
+    gib_kib = (1 << 30) / 1024
+    f_factor, w_factor = gib_kib / fe[ck][0], gib_kib / wr[ck][0]
+    f_kib = sum(fe[kk][1:]) / len(fe[kk][1:])  # the first launch is a warm-up
+    w_kib = sum(wr[kk][1:]) / len(wr[kk][1:])
+    fetch_b, write_b = f_kib * 1024 * f_factor, w_kib * 1024 * w_factor
+    text = f"""# HBM traffic per launch of {kk} (workload lvx_2k_128k, mode {mode})
+# from two rocprofv3 counter passes (FETCH_SIZE, then WRITE_SIZE), KiB per dispatch,
+# each scaled by what the same counter reads for a plain 1 GiB copy kernel
+# (dst.copy_(src) of 2^29 bf16 elements, run by --copy-calibration in the same process).
+# commands (from /tmp, one pass each; then this file is written by
+#   python bench.py --mode {mode} --summarize-traffic <fetch_dir> <write_dir>):
+#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -o run -- {command}
+#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -o run -- {command}
+# raw: FETCH_SIZE {f_kib:.0f} KiB/launch; copy kernel FETCH_SIZE {fe[ck][0]:.0f} KiB for 1048576 KiB moved
+#      WRITE_SIZE {w_kib:.0f} KiB/launch; copy kernel WRITE_SIZE {wr[ck][0]:.0f} KiB for 1048576 KiB moved
+kernel={kk}
+mode={mode}
+kernel_hash={kernel_source_hash()}
+fetch_factor={f_factor:.4f}
+write_factor={w_factor:.4f}
+fetch_bytes_per_launch={fetch_b:.0f}
+write_bytes_per_launch={write_b:.0f}
+hbm_bytes_per_launch={fetch_b + write_b:.0f}
+"""
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write(text)
+    return text
+
+
+def summarize_stats(stats_dir: str, workload: str, command: str, top: int = 8) -> str:
+    """Write profiles/kernels_<workload>.txt from a rocprofv3 --kernel-trace --stats run."""
+    import csv
+    rows = list(csv.DictReader(open(_find(stats_dir, "kernel_stats.csv"))))
+    lines = [f"# rocprofv3 kernel statistics, workload {workload}",
+             f"# command (from /tmp): rocprofv3 --kernel-trace --stats --output-format csv "
+             f"-d <dir> -o run -- {command}",
+             "# columns: calls, average us, total ms, percent of GPU time, kernel"]
+    for r in rows[:top]:
+        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:12.1f} "
+                     f"{float(r['TotalDurationNs']) / 1e6:10.3f} {float(r['Percentage']):6.2f}  "
+                     f"{r['Name'][:160]}")
+    text = "\n".join(lines) + "\n"
+    with open(os.path.join(ROOT, "profiles", f"kernels_{workload}.txt"), "w") as f:
+        f.write(text)
+    return text
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -90,7 +162,21 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy one 1 GiB buffer (a plain copy kernel of "
                          "known size, to calibrate HBM byte counters taken under a profiler)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the profiles/ traffic summary from two rocprofv3 counter passes "
+                         "and exit (no GPU use)")
+    ap.add_argument("--summarize-stats", metavar="STATS_DIR",
+                    help="write profiles/kernels_<workload>.txt from a rocprofv3 --stats run "
+                         "and exit (no GPU use)")
+    ap.add_argument("--profiled-command", default="python3 bench.py",
+                    help="the command line the summarized profiler runs used")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        print(summarize_traffic(*args.summarize_traffic, args.mode, args.profiled_command))
+        return
+    if args.summarize_stats:
+        print(summarize_stats(args.summarize_stats, args.workload, args.profiled_command))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -208,7 +294,7 @@ def main():
         traffic = read_traffic(args.mode) if args.workload == "lvx_2k_128k" else None
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                    "traffic": traffic, "kernel": "fwd_bf16_kernel<128,8,64>",
+                    "traffic": traffic, "kernel": "fwd_bf16_kernel<128>",
                     "launches_per_step": launches,
                     "kernel_ms_per_launch": round(fwd_ms / launches, 4),
                     "other_ms_per_step": round(ms - fwd_ms, 4)}
