@@ -125,10 +125,12 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- dK, dV (KV-stationary)
 
-constexpr int kBwdWaves = 4;
+// dK/dV: 4 waves (one per SIMD: K, V, dK, dV of 32 keys per wave need more
+// than half the register file); dQ: 8 waves, two per SIMD.
+constexpr int kDkdvWaves = 4, kDqWaves = 8;
 
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
-  constexpr int NW = kBwdWaves, BQ = 32, BK = 32 * NW;
+__global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int NW = kDkdvWaves, BQ = 32, BK = 32 * NW;
   constexpr int RM = BQ * KSTR, TR = BQ * D;
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * (2 * RM + 2 * TR)];
   __shared__ float s_lse[2][BQ], s_dlt[2][BQ];
@@ -202,6 +204,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   u32x4 stg[4];
   float st_l = 0.f, st_d = 0.f;
   auto load = [&](int64_t q0, int64_t q1) {
+    if (tid >= 256) return;  // 256 staging threads: Q rows, then dO rows
     const int item = tid & 127;
     const int quad = item / 16, col8 = item % 16;
     const bf16* src = tid < 128 ? qg : dog;
@@ -219,6 +222,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     }
   };
   auto store = [&](int buf) {
+    if (tid >= 256) return;
     bf16* base = smem + buf * (2 * RM + 2 * TR);
     const int item = tid & 127;
     const int quad = item / 16, col8 = item % 16;
@@ -327,8 +331,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- dQ (Q-stationary)
 
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
-  constexpr int NW = kBwdWaves, BN = 32, BM = 32 * NW;
+__global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdParams p) {
+  constexpr int NW = kDqWaves, BN = 32, BM = 32 * NW;
   constexpr int RM = BN * KSTR, TR = BN * D;
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * (2 * RM + TR)];
 
@@ -402,6 +406,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
 
   u32x4 stg[4];
   auto load = [&](int64_t k0, int64_t k1) {
+    if (tid >= 256) return;  // 256 staging threads: K rows, then V rows
     if (tid < 128) {
       const int quad = tid / 16, col8 = tid % 16;
 #pragma unroll
@@ -420,6 +425,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
     }
   };
   auto store = [&](int buf) {
+    if (tid >= 256) return;
     bf16* base = smem + buf * (2 * RM + TR);
     if (tid < 128) {
       put_rows(base, base + 2 * RM, tid / 16, tid % 16, stg);
@@ -591,7 +597,7 @@ hipError_t bwd_run(const BwdArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  const int BK = 32 * kBwdWaves, BM = 32 * kBwdWaves;
+  const int BK = 32 * kDkdvWaves, BM = 32 * kDqWaves;
   const int kv_tiles = (int)(((p.SKV + p.n - 1) / p.n + BK - 1) / BK);
   const int q_tiles = (int)(((p.SQ + p.n - 1) / p.n + BM - 1) / BM);
   const int groups = (int)(BH * p.n);
@@ -600,10 +606,10 @@ hipError_t bwd_run(const BwdArgs& a, hipStream_t st) {
     p.round = r;
     p.groups = groups;
     p.tiles = kv_tiles;
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(xcd_grid_size(kv_tiles, groups)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(xcd_grid_size(kv_tiles, groups)), dim3(64 * kDkdvWaves), 0, st, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     p.tiles = q_tiles;
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3(xcd_grid_size(q_tiles, groups)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3(xcd_grid_size(q_tiles, groups)), dim3(64 * kDqWaves), 0, st, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (p.mode == MODE_ROUNDS) {

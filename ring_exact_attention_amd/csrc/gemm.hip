@@ -12,21 +12,19 @@
 // stores them as one 8-byte write into the [B, H, S, D] output.  Both
 // operands keep the contraction index e contiguous in memory and in LDS.
 //
-// Tiling: 256 (n) x 128 (s) per workgroup of 4 waves (2 x 2), 128 x 64 per
-// wave (4 x 2 MFMA blocks, fp32 accumulators), BK = 32 per LDS stage, double
-// buffered.  Workgroups that share a y tile are placed consecutively on one
-// XCD so the tile is read from HBM once and served from that XCD's L2.
+// Tiling: 256 (n) x 256 (s) per workgroup of 8 waves (2 x 4, two per SIMD),
+// 128 x 64 per wave (4 x 2 MFMA blocks, fp32 accumulators), 64 e per LDS
+// stage (128 contiguous bytes per row and load), double buffered in 144 KB of
+// LDS with rows padded by 16 bytes (conflict-free 16-byte operand reads).
+// Workgroups that share a y tile are placed consecutively on one XCD so the
+// tile is read from HBM once and served from that XCD's L2; W (both
+// projections, 64 MB) stays in the MALL.
 #include "bwa.h"
 #include "common.h"
 
 namespace bwa {
 
 namespace {
-
-constexpr int GM = 256;  // n per workgroup
-constexpr int GN = 128;  // s per workgroup
-constexpr int GK = 32;   // e per stage
-constexpr int GS = GK + 8;  // LDS row stride (elements), 16 B pad
 
 struct GemmParams {
   const bf16* y;     // [B*S, E]
@@ -44,11 +42,27 @@ __device__ inline uint32_t pk(float a, float b) {
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void gemm_kv_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) bf16 As[2][GM * GS];
-  __shared__ __attribute__((aligned(16))) bf16 Bs[2][GN * GS];
+// Tiling: GM x GN per workgroup of WM x WN waves, GK per LDS stage.
+template <int GM_, int GN_, int GK_, int WM_, int WN_>
+struct GemmTile {
+  static constexpr int GM = GM_, GN = GN_, GK = GK_, WM = WM_, WN = WN_;
+  static constexpr int NW = WM * WN, NT = 64 * NW;
+  static constexpr int WTM = GM / WM, WTN = GN / WN;  // per-wave tile (n x s)
+  static constexpr int FA = WTM / 32, FB = WTN / 32;  // 32x32 MFMA blocks per wave
+  static constexpr int GS = GK + 8;                   // LDS row stride (elements)
+  static constexpr int A_EL = GM * GS, B_EL = GN * GS;
+  static constexpr int CPR = GK / 8;                  // 16-byte chunks per row
+  static constexpr int KC = (GM + GN) * CPR / NT;     // chunks per thread per stage
+  static_assert(KC * NT == (GM + GN) * CPR, "staging must divide evenly");
+  static_assert((GM * CPR) % NT == 0, "A chunks must fill whole passes");
+};
 
-  // groups = (projection, s tile); tiles = n tiles sharing that y tile
+template <typename T>
+__global__ __launch_bounds__(T::NT) void gemm_kv_kernel(GemmParams p) {
+  constexpr int GM = T::GM, GN = T::GN, GK = T::GK, GS = T::GS, CPR = T::CPR, KC = T::KC;
+  constexpr int KA = GM * CPR / T::NT;  // passes of A chunks
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * (T::A_EL + T::B_EL)];
+
   int grp, nt;
   if (!xcd_group_tile(blockIdx.x, p.n_tiles, 2 * p.s_tiles, &grp, &nt)) return;
   const int proj = grp / p.s_tiles;
@@ -56,39 +70,48 @@ __global__ __launch_bounds__(256) void gemm_kv_kernel(GemmParams p) {
   const int n0 = nt * GM, s0 = st * GN;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / T::WN, wn = wave % T::WN;
   const bf16* wsrc = p.w[proj];
 
-  u32x4 stg[6];
+  // thread's chunks: passes i < KA are W rows, the rest y rows; 8-lane groups
+  // cover one row's GK elements (128 contiguous bytes for GK = 64)
+  u32x4 stg[KC];
   auto load = [&](int e0) {
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      int c = tid + 256 * i;     // 1536 chunks: 1024 from W (256 rows), then 512 from y (128 rows)
-      int row = c < 1024 ? (c >> 2) : ((c - 1024) >> 2), col8 = c & 3;
-      if (c < 1024) {
-        int n = n0 + row;
-        stg[i] = n < p.HD ? *(const u32x4*)(wsrc + (int64_t)n * p.E + e0 + col8 * 8) : u32x4{};
+    for (int i = 0; i < KC; ++i) {
+      const int c = tid + T::NT * i;
+      if (i < KA) {
+        const int row = c / CPR, col8 = c % CPR;
+        const int n = min(n0 + row, p.HD - 1);
+        stg[i] = *(const u32x4*)(wsrc + (int64_t)n * p.E + e0 + col8 * 8);
       } else {
-        int s = s0 + row;
-        stg[i] = s < p.BS ? *(const u32x4*)(p.y + (int64_t)s * p.E + e0 + col8 * 8) : u32x4{};
+        const int cb = c - GM * CPR;
+        const int row = cb / CPR, col8 = cb % CPR;
+        const int sr = min(s0 + row, p.BS - 1);
+        stg[i] = *(const u32x4*)(p.y + (int64_t)sr * p.E + e0 + col8 * 8);
       }
     }
   };
   auto store = [&](int buf) {
+    bf16* As = smem + buf * (T::A_EL + T::B_EL);
+    bf16* Bs = As + T::A_EL;
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      int c = tid + 256 * i;
-      int row = c < 1024 ? (c >> 2) : ((c - 1024) >> 2), col8 = c & 3;
-      bf16* dst = (c < 1024 ? As[buf] : Bs[buf]) + row * GS + col8 * 8;
-      *(u32x4*)dst = stg[i];
+    for (int i = 0; i < KC; ++i) {
+      const int c = tid + T::NT * i;
+      if (i < KA) {
+        *(u32x4*)(As + (c / CPR) * GS + (c % CPR) * 8) = stg[i];
+      } else {
+        const int cb = c - GM * CPR;
+        *(u32x4*)(Bs + (cb / CPR) * GS + (cb % CPR) * 8) = stg[i];
+      }
     }
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[T::FA][T::FB];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < T::FA; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+    for (int b = 0; b < T::FB; ++b) acc[a][b] = f32x16{};
 
   const int nk = p.E / GK;
   load(0);
@@ -98,19 +121,21 @@ __global__ __launch_bounds__(256) void gemm_kv_kernel(GemmParams p) {
   for (int kt = 0; kt < nk; ++kt) {
     const bool more = kt + 1 < nk;
     if (more) load((kt + 1) * GK);
+    const bf16* As = smem + buf * (T::A_EL + T::B_EL);
+    const bf16* Bs = As + T::A_EL;
 #pragma unroll
     for (int ks = 0; ks < GK / 16; ++ks) {
-      bf16x8 av[4], bv[2];
+      bf16x8 av[T::FA], bv[T::FB];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-        av[a] = *(const bf16x8*)(As[buf] + (wm * 128 + 32 * a + lr) * GS + 16 * ks + 8 * g);
+      for (int a = 0; a < T::FA; ++a)
+        av[a] = *(const bf16x8*)(As + (wm * T::WTM + 32 * a + lr) * GS + 16 * ks + 8 * g);
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-        bv[b] = *(const bf16x8*)(Bs[buf] + (wn * 64 + 32 * b + lr) * GS + 16 * ks + 8 * g);
+      for (int b = 0; b < T::FB; ++b)
+        bv[b] = *(const bf16x8*)(Bs + (wn * T::WTN + 32 * b + lr) * GS + 16 * ks + 8 * g);
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < T::FA; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < T::FB; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
     }
     if (!more) break;
@@ -119,19 +144,17 @@ __global__ __launch_bounds__(256) void gemm_kv_kernel(GemmParams p) {
     buf ^= 1;
   }
 
-  // C^T block (a, b): lane column s = s0 + wn*64 + 32b + lr,
-  // rows n = n0 + wm*128 + 32a + 8i + 4g + j  (j = 0..3 consecutive head dims)
   bf16* out = p.out[proj];
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int s = s0 + wn * 64 + 32 * b + lr;
+  for (int b = 0; b < T::FB; ++b) {
+    const int s = s0 + wn * T::WTN + 32 * b + lr;
     if (s >= p.BS) continue;
     const int bb = s / p.S, si = s % p.S;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < T::FA; ++a)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int n = n0 + wm * 128 + 32 * a + 8 * i + 4 * g;
+        const int n = n0 + wm * T::WTM + 32 * a + 8 * i + 4 * g;
         if (n >= p.HD) continue;
         const int hh = n / p.D, d = n % p.D;
         bf16* dst = out + bb * p.so[proj][0] + hh * p.so[proj][1] + (int64_t)si * p.so[proj][2] + d;
@@ -139,6 +162,16 @@ __global__ __launch_bounds__(256) void gemm_kv_kernel(GemmParams p) {
                              pk(acc[a][b][4 * i + 2], acc[a][b][4 * i + 3])};
       }
   }
+}
+
+using KvTile = GemmTile<256, 256, 64, 2, 4>;
+
+template <typename T>
+static void launch_gemm(GemmParams p, hipStream_t st) {
+  p.n_tiles = (p.HD + T::GM - 1) / T::GM;
+  p.s_tiles = (p.BS + T::GN - 1) / T::GN;
+  const int blocks = xcd_grid_size(p.n_tiles, 2 * p.s_tiles);
+  hipLaunchKernelGGL(gemm_kv_kernel<T>, dim3(blocks), dim3(T::NT), 0, st, p);
 }
 
 hipError_t gemm_kv_launch(const void* y, const void* wk_t, const void* wv_t, int64_t B, int64_t S,
@@ -158,10 +191,7 @@ hipError_t gemm_kv_launch(const void* y, const void* wk_t, const void* wv_t, int
   p.D = (int)Dh;
   p.HD = (int)(H * Dh);
   p.BS = (int)(B * S);
-  p.n_tiles = (p.HD + GM - 1) / GM;
-  p.s_tiles = (p.BS + GN - 1) / GN;
-  int blocks = xcd_grid_size(p.n_tiles, 2 * p.s_tiles);
-  hipLaunchKernelGGL(gemm_kv_kernel, dim3(blocks), dim3(256), 0, st, p);
+  launch_gemm<KvTile>(p, st);
   return hipGetLastError();
 }
 
