@@ -15,6 +15,8 @@
 // is a v_mfma_f32_32x32x16_bf16; operands whose contraction index is the
 // row index of their storage (dO^T, Q^T, K^T) are staged in LDS as
 // [row/4][d][4] so that four consecutive rows of one column are 8 bytes.
+#include <type_traits>
+
 #include "bwd_args.h"
 #include "common.h"
 
@@ -124,13 +126,19 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- dK, dV (KV-stationary)
+//
+// 128 keys per workgroup, 8 waves: waves 0-3 compute dV and waves 4-7 dK for
+// the same four 32-key groups (wave w and w+4 share a SIMD).  Splitting by
+// output keeps each wave under half the register file (dV: K and dV; dK: K, V
+// and dK), so two waves run per SIMD; the price is that S is computed by both
+// roles (40 instead of 32 MFMAs per 32 x 32 block).  Queries stream in steps
+// of 64 rows, staged by the dV waves.
 
-// dK/dV: 4 waves (one per SIMD: K, V, dK, dV of 32 keys per wave need more
-// than half the register file); dQ: 8 waves, two per SIMD.
-constexpr int kDkdvWaves = 4, kDqWaves = 8;
+// dK/dV: 8 waves in two roles; dQ: 8 waves, two per SIMD.
+constexpr int kDkdvWaves = 8, kDqWaves = 8;
 
 __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) {
-  constexpr int NW = kDkdvWaves, BQ = 32, BK = 32 * NW;
+  constexpr int BQ = 64, BK = 128;
   constexpr int RM = BQ * KSTR, TR = BQ * D;
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * (2 * RM + 2 * TR)];
   __shared__ float s_lse[2][BQ], s_dlt[2][BQ];
@@ -158,7 +166,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
   const int b = bh / p.H, h = bh % p.H;
-  const int64_t kw0 = kt0 + wave * 32;
+  const int64_t kw0 = kt0 + (wave & 3) * 32;
   const int64_t mykey = kw0 + lr;
   const bool key_ok = mykey < kt1;
 
@@ -166,20 +174,6 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
   const bf16* dog = p.dout + b * p.sdo[0] + h * p.sdo[1];
   const float* lseg = p.lse + (int64_t)bh * p.SQ;
   const float* dltg = p.delta + (int64_t)bh * p.SQ;
-
-  bf16x8 kreg[D / 16], vreg[D / 16];
-  {
-    const bf16* kp = p.k + b * p.sk[0] + h * p.sk[1] + mykey * p.sk[2];
-    const bf16* vp = p.v + b * p.sv[0] + h * p.sv[1] + mykey * p.sv[2];
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      kreg[s] = key_ok ? *(const bf16x8*)(kp + 16 * s + 8 * g) : bf16x8{};
-      vreg[s] = key_ok ? *(const bf16x8*)(vp + 16 * s + 8 * g) : bf16x8{};
-    }
-  }
-  f32x16 dk[D / 32], dv[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) { dk[dt] = f32x16{}; dv[dt] = f32x16{}; }
 
   // q-step iterator over the ordered segments
   int r = 0;
@@ -201,18 +195,19 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
   seek(0);
   if (r >= nseg && acc_in) return;  // nothing to add this round
 
-  u32x4 stg[4];
+  // staging by the dV waves (threads 0-255): each moves the same 4-row x
+  // 8-column block of Q and of dO
+  u32x4 stg[8];
   float st_l = 0.f, st_d = 0.f;
   auto load = [&](int64_t q0, int64_t q1) {
-    if (tid >= 256) return;  // 256 staging threads: Q rows, then dO rows
-    const int item = tid & 127;
-    const int quad = item / 16, col8 = item % 16;
-    const bf16* src = tid < 128 ? qg : dog;
-    const int64_t ss = tid < 128 ? p.sq[2] : p.sdo[2];
+    if (tid >= 256) return;
+    const int quad = tid / 16, col8 = tid % 16;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      int64_t row = q0 + 4 * quad + rr;
-      stg[rr] = row < q1 ? *(const u32x4*)(src + row * ss + col8 * 8) : u32x4{};
+      const int64_t row = q0 + 4 * quad + rr;
+      const bool ok = row < q1;
+      stg[rr] = ok ? *(const u32x4*)(qg + row * p.sq[2] + col8 * 8) : u32x4{};
+      stg[4 + rr] = ok ? *(const u32x4*)(dog + row * p.sdo[2] + col8 * 8) : u32x4{};
     }
     if (tid < BQ) {
       int64_t row = q0 + tid;
@@ -224,109 +219,128 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
   auto store = [&](int buf) {
     if (tid >= 256) return;
     bf16* base = smem + buf * (2 * RM + 2 * TR);
-    const int item = tid & 127;
-    const int quad = item / 16, col8 = item % 16;
-    if (tid < 128) put_rows(base, base + 2 * RM, quad, col8, stg);
-    else put_rows(base + RM, base + 2 * RM + TR, quad, col8, stg);
+    const int quad = tid / 16, col8 = tid % 16;
+    put_rows(base, base + 2 * RM, quad, col8, stg);
+    put_rows(base + RM, base + 2 * RM + TR, quad, col8, stg + 4);
     if (tid < BQ) { s_lse[buf][tid] = st_l; s_dlt[buf][tid] = st_d; }
   };
 
-  int buf = 0;
   if (r < nseg) { load(qc, qend); store(0); }
   __syncthreads();
   const float c2 = p.scale_log2;
-  while (r < nseg) {
-    const int64_t q0 = qc, q1 = qend;
-    // advance
-    int64_t nq0 = 0, nq1 = 0;
-    bool more;
+
+  // One role's whole loop: IS_DK selects dK (needs V) or dV.
+  auto run = [&](auto role) __attribute__((always_inline)) {
+    constexpr bool IS_DK = decltype(role)::value;
+    bf16x8 kreg[D / 16], vreg[IS_DK ? D / 16 : 1];
     {
-      int64_t nx = qc + BQ;
-      if (nx < qend) { more = true; nq0 = nx; nq1 = qend; qc = nx; }
-      else { seek(r + 1); more = r < nseg; nq0 = qc; nq1 = qend; }
-    }
-    if (more) load(nq0, nq1);
-
-    const bf16* base = smem + buf * (2 * RM + 2 * TR);
-    const bf16* Qs = base;
-    const bf16* Ds = base + RM;
-    const bf16* Qt = base + 2 * RM;
-    const bf16* Dt = base + 2 * RM + TR;
-
-    f32x16 sacc = f32x16{}, pacc = f32x16{};
+      const bf16* kp = p.k + b * p.sk[0] + h * p.sk[1] + mykey * p.sk[2];
+      const bf16* vp = p.v + b * p.sv[0] + h * p.sv[1] + mykey * p.sv[2];
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      bf16x8 aq = *(const bf16x8*)(Qs + lr * KSTR + 16 * s + 8 * g);
-      bf16x8 ad = *(const bf16x8*)(Ds + lr * KSTR + 16 * s + 8 * g);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[s], sacc, 0, 0, 0);
-      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vreg[s], pacc, 0, 0, 0);
-    }
-    // element 4i+j is query q0 + 8i + 4g + j; this lane's key is mykey
-    const bool need_mask = p.causal && (q0 < kw0 + 31);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f32x4 l4 = *(const f32x4*)(&s_lse[buf][8 * i + 4 * g]);
-      f32x4 d4 = *(const f32x4*)(&s_dlt[buf][8 * i + 4 * g]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * i + j], c2, -l4[j]));
-        if (need_mask && mykey > q0 + 8 * i + 4 * g + j) pv = 0.f;
-        sacc[4 * i + j] = pv;                         // P
-        pacc[4 * i + j] = pv * (pacc[4 * i + j] - d4[j]);  // dS (unscaled)
+      for (int s = 0; s < D / 16; ++s) {
+        kreg[s] = key_ok ? *(const bf16x8*)(kp + 16 * s + 8 * g) : bf16x8{};
+        if constexpr (IS_DK) vreg[s] = key_ok ? *(const bf16x8*)(vp + 16 * s + 8 * g) : bf16x8{};
       }
     }
+    f32x16 acc[D / 32];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      bf16x8 pb = pack8(sacc, hh), sb = pack8(pacc, hh);
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(Dt, hh, dt, lr, g), pb, dv[dt],
-                                                         0, 0, 0);
-        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(Qt, hh, dt, lr, g), sb, dk[dt],
-                                                         0, 0, 0);
-      }
-    }
-    (void)q1;
-    if (!more) break;
-    store(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-  }
+    for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
 
-  if (!key_ok) return;
-  const float sc = p.scale;
-  if (p.mode == MODE_ROUNDS) {
-    float* dkp = p.dk_acc + ((int64_t)bh * p.SKV + mykey) * D;
-    float* dvp = p.dv_acc + ((int64_t)bh * p.SKV + mykey) * D;
+    int buf = 0;
+    while (r < nseg) {
+      const int64_t q0 = qc;
+      int64_t nq0 = 0, nq1 = 0;
+      bool more;
+      {
+        int64_t nx = qc + BQ;
+        if (nx < qend) { more = true; nq0 = nx; nq1 = qend; qc = nx; }
+        else { seek(r + 1); more = r < nseg; nq0 = qc; nq1 = qend; }
+      }
+      if (!IS_DK && more) load(nq0, nq1);
+
+      const bf16* base = smem + buf * (2 * RM + 2 * TR);
+      const bf16* Qs = base;
+      const bf16* Ds = base + RM;
+      const bf16* Qt = base + 2 * RM;
+      const bf16* Dt = base + 2 * RM + TR;
+
+      // the two 32-query halves one after the other (keeps the live score
+      // tiles to one S and one dP block per wave)
+      const bool need_mask = p.causal && (q0 < kw0 + 31);
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+      for (int qh = 0; qh < BQ / 32; ++qh) {
+        f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = 32 * dt + 8 * i + 4 * g;
-        f32x4 a = f32x4{dk[dt][4 * i] * sc, dk[dt][4 * i + 1] * sc, dk[dt][4 * i + 2] * sc,
-                        dk[dt][4 * i + 3] * sc};
-        f32x4 c = f32x4{dv[dt][4 * i], dv[dt][4 * i + 1], dv[dt][4 * i + 2], dv[dt][4 * i + 3]};
-        if (acc_in) {
-          a += *(const f32x4*)(dkp + d);
-          c += *(const f32x4*)(dvp + d);
+        for (int s = 0; s < D / 16; ++s) {
+          bf16x8 aq = *(const bf16x8*)(Qs + (32 * qh + lr) * KSTR + 16 * s + 8 * g);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[s], sacc, 0, 0, 0);
+          if constexpr (IS_DK) {
+            bf16x8 ad = *(const bf16x8*)(Ds + (32 * qh + lr) * KSTR + 16 * s + 8 * g);
+            pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vreg[s], pacc, 0, 0, 0);
+          }
         }
-        *(f32x4*)(dkp + d) = a;
-        *(f32x4*)(dvp + d) = c;
-      }
-  } else {
-    bf16* dkp = p.dk + b * p.sdk[0] + h * p.sdk[1] + mykey * p.sdk[2];
-    bf16* dvp = p.dv + b * p.sdv[0] + h * p.sdv[1] + mykey * p.sdv[2];
+        // element 4i+j is query q0 + 32qh + 8i + 4g + j; this lane's key is mykey
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+        for (int i = 0; i < 4; ++i) {
+          const int qo = 32 * qh + 8 * i + 4 * g;
+          f32x4 l4 = *(const f32x4*)(&s_lse[buf][qo]);
+          f32x4 d4 = *(const f32x4*)(&s_dlt[buf][qo]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = 32 * dt + 8 * i + 4 * g;
-        *(u32x2*)(dkp + d) = u32x2{pk_bf16(dk[dt][4 * i] * sc, dk[dt][4 * i + 1] * sc),
-                                   pk_bf16(dk[dt][4 * i + 2] * sc, dk[dt][4 * i + 3] * sc)};
-        *(u32x2*)(dvp + d) = u32x2{pk_bf16(dv[dt][4 * i], dv[dt][4 * i + 1]),
-                                   pk_bf16(dv[dt][4 * i + 2], dv[dt][4 * i + 3])};
+          for (int j = 0; j < 4; ++j) {
+            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * i + j], c2, -l4[j]));
+            if (need_mask && mykey > q0 + qo + j) pv = 0.f;
+            if constexpr (IS_DK)
+              sacc[4 * i + j] = pv * (pacc[4 * i + j] - d4[j]);  // dS (unscaled)
+            else
+              sacc[4 * i + j] = pv;  // P
+          }
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const bf16x8 xb = pack8(sacc, hh);
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt)
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                tr_operand(IS_DK ? Qt : Dt, 2 * qh + hh, dt, lr, g), xb, acc[dt], 0, 0, 0);
+        }
       }
-  }
+      if (!more) break;
+      if constexpr (!IS_DK) store(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    }
+
+    if (!key_ok) return;
+    const float sc = IS_DK ? p.scale : 1.f;
+    if (p.mode == MODE_ROUNDS) {
+      float* dst = (IS_DK ? p.dk_acc : p.dv_acc) + ((int64_t)bh * p.SKV + mykey) * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = 32 * dt + 8 * i + 4 * g;
+          f32x4 a = f32x4{acc[dt][4 * i] * sc, acc[dt][4 * i + 1] * sc, acc[dt][4 * i + 2] * sc,
+                          acc[dt][4 * i + 3] * sc};
+          if (acc_in) a += *(const f32x4*)(dst + d);
+          *(f32x4*)(dst + d) = a;
+        }
+    } else {
+      bf16* dst = IS_DK ? p.dk + b * p.sdk[0] + h * p.sdk[1] + mykey * p.sdk[2]
+                        : p.dv + b * p.sdv[0] + h * p.sdv[1] + mykey * p.sdv[2];
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = 32 * dt + 8 * i + 4 * g;
+          *(u32x2*)(dst + d) = u32x2{pk_bf16(acc[dt][4 * i] * sc, acc[dt][4 * i + 1] * sc),
+                                     pk_bf16(acc[dt][4 * i + 2] * sc, acc[dt][4 * i + 3] * sc)};
+        }
+    }
+  };
+  if (wave >= 4)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 }
 
 // ---------------------------------------------------------------- dQ (Q-stationary)
@@ -597,7 +611,7 @@ hipError_t bwd_run(const BwdArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  const int BK = 32 * kDkdvWaves, BM = 32 * kDqWaves;
+  const int BK = 128, BM = 32 * kDqWaves;
   const int kv_tiles = (int)(((p.SKV + p.n - 1) / p.n + BK - 1) / BK);
   const int q_tiles = (int)(((p.SQ + p.n - 1) / p.n + BM - 1) / BM);
   const int groups = (int)(BH * p.n);
