@@ -207,6 +207,33 @@ bwa_status bwa_kv_recompute(const void* y, const void* wk_t, const void* wv_t, i
                             int64_t S_KV, int64_t E, int64_t H, int64_t D, int32_t dtype,
                             const bwa_tensor* k, const bwa_tensor* v, void* stream);
 
+/*
+ * Per-round cost model of the two ring schedules and the choice between them
+ * (LV-XAttn review, "What carries the argument": the per-round runtime
+ * identity).  With d = H*D the model width, a round of either schedule
+ * computes one block pair, f = 4 * (S_Q/n) * (S_KV/n) * d FLOP (two
+ * contractions, a multiply-add counted as 2), and sends one message that the
+ * model takes to overlap the compute, so a round lasts max(compute, comm):
+ *   KV-stationary (LV-XAttn): 2*S_Q*d/n + S_Q/n elements (Q_i, O_i, L_i);
+ *   Q-stationary (Ring):      2*S_KV*d/n elements (K_i, V_i).
+ * Times: compute = f / flops_per_s, comm = elements * elem_bytes / bytes_per_s.
+ * *choice receives the schedule with the shorter round (KV-stationary on a
+ * tie); *model, if not NULL, receives the five times in seconds.
+ * All sizes and rates must be positive (BWA_ERR_INVALID_ARG otherwise).
+ * Host-only: enqueues nothing and needs no GPU.
+ */
+typedef struct {
+  double t_compute;                /* f / flops_per_s */
+  double t_comm_kv_stationary;     /* LV-XAttn message */
+  double t_comm_q_stationary;      /* Ring message */
+  double t_round_kv_stationary;    /* max(t_compute, t_comm_kv_stationary) */
+  double t_round_q_stationary;     /* max(t_compute, t_comm_q_stationary) */
+} bwa_schedule_model;
+
+bwa_status bwa_choose_schedule(int64_t S_Q, int64_t S_KV, int64_t d_model, int32_t n,
+                               double flops_per_s, double bytes_per_s, int32_t elem_bytes,
+                               int32_t* choice, bwa_schedule_model* model);
+
 /* Static string naming a status code. */
 const char* bwa_status_string(bwa_status s);
 /* Detail of the calling thread's last failing call ("" if none). */

@@ -73,6 +73,8 @@ def _load():
         lib.orc_attn_bwd_heads.argtypes = [vp, vp, vp, vp, ci, ci, i64, i64, i64, i64, i64, f64,
                                            ci, vp, i64, vp, i64, vp, vp, vp, vp, vp]
         lib.orc_kv_proj_rows.argtypes = [vp, vp, ci, i64, i64, i64, i64, vp, i64, vp]
+        lib.orc_schedule_model.argtypes = [f64] * 7 + [vp]
+        lib.orc_schedule_model.restype = ci
         _lib = lib
     return _lib
 
@@ -264,3 +266,15 @@ def kv_proj(y, w_t, H: int, D: int, rows=None):
     if rows is None:
         return out.reshape(B, S, H, D).transpose(0, 2, 1, 3).copy()
     return out
+
+
+def schedule_model(S_Q, S_KV, d, n, flops_per_s, bytes_per_s, elem_bytes=2):
+    """Per-round cost model of the two schedules (LV-XAttn review, "What
+    carries the argument").  Returns ("kv" | "q", {compute, comm_kv, comm_q,
+    round_kv, round_q} in seconds); "kv" (LV-XAttn) wins ties."""
+    out = np.zeros(5, dtype=np.float64)
+    c = _load().orc_schedule_model(float(S_Q), float(S_KV), float(d), float(n),
+                                   float(flops_per_s), float(bytes_per_s), float(elem_bytes),
+                                   out.ctypes.data)
+    keys = ("compute", "comm_kv", "comm_q", "round_kv", "round_q")
+    return ("kv" if c == 0 else "q"), dict(zip(keys, out.tolist()))

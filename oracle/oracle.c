@@ -335,3 +335,30 @@ void orc_kv_proj_rows(const void* y, const void* w_t, int dt, int64_t B, int64_t
     }
   }
 }
+
+/* ------------------------------------------------------------------------
+ * Per-round cost model of the two ring schedules ([LVX] "What carries the
+ * argument": a round lasts max(f(S_Q d/n, S_KV d/n), comm(message)), with
+ * message 2 S_Q d/n + S_Q/n elements for LV-XAttn (Q_i, O_i, L_i) and
+ * 2 S_KV d/n elements for Ring Attention (K_i, V_i)).
+ * Reading: f is the FLOP count of one block pair, two contractions of a
+ * (S_Q/n x d) block with a (S_KV/n x d) block, a multiply-add counted as 2;
+ * comm(x) = x * elem_bytes / bytes_per_s.  out = {compute, comm_lv,
+ * comm_ring, round_lv, round_ring} seconds; returns 0 (LV-XAttn) when its
+ * round is not longer, else 1 (Ring). */
+int orc_schedule_model(double S_Q, double S_KV, double d, double n, double flops_per_s,
+                       double bytes_per_s, double elem_bytes, double* out) {
+  double q_block = S_Q / n, kv_block = S_KV / n;
+  double f = 2.0 * (2.0 * q_block * kv_block * d); /* S = Q K^T, then P V */
+  double lv_elems = 2.0 * S_Q * d / n + S_Q / n;
+  double ring_elems = 2.0 * S_KV * d / n;
+  double t_f = f / flops_per_s;
+  double t_lv = lv_elems * elem_bytes / bytes_per_s;
+  double t_ring = ring_elems * elem_bytes / bytes_per_s;
+  out[0] = t_f;
+  out[1] = t_lv;
+  out[2] = t_ring;
+  out[3] = t_f > t_lv ? t_f : t_lv;
+  out[4] = t_f > t_ring ? t_f : t_ring;
+  return out[3] <= out[4] ? 0 : 1;
+}

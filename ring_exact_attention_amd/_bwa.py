@@ -28,8 +28,16 @@ MODES = {"rounds": MODE_ROUNDS, "fused": MODE_FUSED, "split": MODE_SPLIT}
 
 EXPORTED = ("bwa_partial_fwd", "bwa_merge", "bwa_merge_partials", "bwa_ring_fwd_workspace",
             "bwa_ring_fwd",
-            "bwa_ring_bwd_workspace", "bwa_ring_bwd", "bwa_kv_recompute", "bwa_status_string",
+            "bwa_ring_bwd_workspace", "bwa_ring_bwd", "bwa_kv_recompute", "bwa_choose_schedule",
+            "bwa_status_string",
             "bwa_last_error", "bwa_version")
+
+
+class ScheduleModel(ctypes.Structure):
+    _fields_ = [("t_compute", ctypes.c_double), ("t_comm_kv_stationary", ctypes.c_double),
+                ("t_comm_q_stationary", ctypes.c_double),
+                ("t_round_kv_stationary", ctypes.c_double),
+                ("t_round_q_stationary", ctypes.c_double)]
 
 
 class BwaError(RuntimeError):
@@ -73,6 +81,11 @@ def lib():
         for name in ("bwa_partial_fwd", "bwa_merge", "bwa_merge_partials", "bwa_ring_fwd",
                      "bwa_ring_bwd", "bwa_kv_recompute"):
             getattr(L, name).restype = ci
+        L.bwa_choose_schedule.argtypes = [i64, i64, i64, ctypes.c_int32, ctypes.c_double,
+                                          ctypes.c_double, ctypes.c_int32,
+                                          ctypes.POINTER(ctypes.c_int32),
+                                          ctypes.POINTER(ScheduleModel)]
+        L.bwa_choose_schedule.restype = ci
         L.bwa_status_string.argtypes = [ci]
         L.bwa_status_string.restype = ctypes.c_char_p
         L.bwa_last_error.restype = ctypes.c_char_p
@@ -261,3 +274,15 @@ def bwa_kv_recompute(y, wk_t, wv_t, H, D, k=None, v=None):
                                   _dtype_code(y.dtype), ctypes.byref(tk), ctypes.byref(tv),
                                   _stream(y.device)))
     return k, v
+
+
+def bwa_choose_schedule(S_Q, S_KV, d_model, n, flops_per_s, bytes_per_s, elem_bytes=2):
+    """Schedule with the shorter modelled round ("kv": LV-XAttn, "q": Ring) and
+    the model's times in seconds.  Host-only."""
+    L = lib()
+    choice = ctypes.c_int32(-1)
+    m = ScheduleModel()
+    _check(L.bwa_choose_schedule(S_Q, S_KV, d_model, n, float(flops_per_s), float(bytes_per_s),
+                                 elem_bytes, ctypes.byref(choice), ctypes.byref(m)))
+    times = {f: getattr(m, f) for f, _ in ScheduleModel._fields_}
+    return ("kv" if choice.value == SCHED_KV_STATIONARY else "q"), times

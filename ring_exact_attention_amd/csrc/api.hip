@@ -170,6 +170,30 @@ const char* bwa_last_error(void) { return g_last_error.c_str(); }
 
 int bwa_version(void) { return BWA_VERSION; }
 
+bwa_status bwa_choose_schedule(int64_t S_Q, int64_t S_KV, int64_t d_model, int32_t n,
+                               double flops_per_s, double bytes_per_s, int32_t elem_bytes,
+                               int32_t* choice, bwa_schedule_model* model) {
+  if (S_Q <= 0 || S_KV <= 0 || d_model <= 0 || n <= 0 || elem_bytes <= 0)
+    return fail(BWA_ERR_INVALID_ARG, "sizes, n and elem_bytes must be positive");
+  if (!(flops_per_s > 0.0) || !(bytes_per_s > 0.0) || flops_per_s == HUGE_VAL ||
+      bytes_per_s == HUGE_VAL)
+    return fail(BWA_ERR_INVALID_ARG, "rates must be positive and finite");
+  if (!choice) return fail(BWA_ERR_INVALID_ARG, "choice is NULL");
+  const double sq = (double)S_Q / n, skv = (double)S_KV / n, d = (double)d_model;
+  bwa_schedule_model m;
+  m.t_compute = 4.0 * sq * skv * d / flops_per_s;
+  m.t_comm_kv_stationary = (2.0 * sq * d + sq) * elem_bytes / bytes_per_s;
+  m.t_comm_q_stationary = 2.0 * skv * d * elem_bytes / bytes_per_s;
+  m.t_round_kv_stationary = m.t_compute > m.t_comm_kv_stationary ? m.t_compute
+                                                                 : m.t_comm_kv_stationary;
+  m.t_round_q_stationary = m.t_compute > m.t_comm_q_stationary ? m.t_compute
+                                                               : m.t_comm_q_stationary;
+  *choice = m.t_round_kv_stationary <= m.t_round_q_stationary ? BWA_SCHED_KV_STATIONARY
+                                                              : BWA_SCHED_Q_STATIONARY;
+  if (model) *model = m;
+  return BWA_OK;
+}
+
 bwa_status bwa_partial_fwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v,
                            int64_t q0, int64_t nq, int64_t k0, int64_t nk, float scale,
                            int causal, float* o_acc, float* lse_acc, int accumulate,

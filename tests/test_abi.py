@@ -180,3 +180,31 @@ def test_product_path_never_touches_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
                 assert "liboracle" not in text and "oracle.c" not in text, f
+
+
+def test_choose_schedule_matches_oracle(L):
+    import oracle
+    grid = [(5514, 15279944, 4096, 16, 312e12, 25e9, 2), (65536, 65536, 4096, 16, 1e18, 1e9, 2),
+            (1_000_000, 4096, 4096, 8, 312e12, 25e9, 2), (8192, 8192, 4096, 2, 1e9, 1e18, 2),
+            (2048, 131072 * 8, 4096, 8, 2.5e15, 153e9, 2), (300, 1000, 128, 4, 1e12, 1e9, 4),
+            (1, 1, 1, 1, 1.0, 1.0, 1)]
+    for args in grid:
+        got, tg = _bwa.bwa_choose_schedule(*args)
+        want, tw = oracle.schedule_model(*args)
+        assert got == want, args
+        for a, b in (("t_compute", "compute"), ("t_comm_kv_stationary", "comm_kv"),
+                     ("t_comm_q_stationary", "comm_q"), ("t_round_kv_stationary", "round_kv"),
+                     ("t_round_q_stationary", "round_q")):
+            assert abs(tg[a] - tw[b]) <= 1e-12 * abs(tw[b]), (args, a)
+
+
+def test_choose_schedule_validation(L):
+    choice = ctypes.c_int32()
+    f = L.bwa_choose_schedule
+    bad = [(0, 10, 8, 2, 1e12, 1e9, 2), (10, -1, 8, 2, 1e12, 1e9, 2), (10, 10, 8, 0, 1e12, 1e9, 2),
+           (10, 10, 8, 2, 0.0, 1e9, 2), (10, 10, 8, 2, 1e12, float("inf"), 2),
+           (10, 10, 8, 2, float("nan"), 1e9, 2), (10, 10, 8, 2, 1e12, 1e9, 0)]
+    for args in bad:
+        assert f(*args, ctypes.byref(choice), None) == _bwa.BWA_ERR_INVALID_ARG, args
+    assert f(10, 10, 8, 2, 1e12, 1e9, 2, None, None) == _bwa.BWA_ERR_INVALID_ARG
+    assert f(10, 10, 8, 2, 1e12, 1e9, 2, ctypes.byref(choice), None) == _bwa.BWA_OK

@@ -434,3 +434,50 @@ def test_projection_vs_numpy(orc):
     K2 = orc.kv_proj(2 * y + 1, w_t, H, D)
     K1 = orc.kv_proj(np.ones_like(y), w_t, H, D)
     np.testing.assert_allclose(K2, 2 * K + K1, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------- schedule cost model
+
+def test_schedule_model_comm_volume_video_mme(orc):
+    """LV-XAttn review, "The paper's central claim": for Llama 3-V on Video-MME
+    (S_Q = 5,514, S_KV = 15,279,944) rotating Q, O and the softmax statistics
+    instead of K, V cuts communication volume to 0.04% of Ring Attention's."""
+    for d in (1024, 4096, 8192):
+        for n in (4, 16, 64):
+            _, t = orc.schedule_model(5514, 15279944, d, n, 312e12, 25e9)
+            ratio = t["comm_kv"] / t["comm_q"]
+            assert round(100 * ratio, 2) == 0.04, (d, n, ratio)
+
+
+def test_schedule_model_speedup_closed_form(orc):
+    """When the LV-XAttn round is compute-bound and the Ring round is
+    communication-bound, the modelled speedup is n * FLOPS / (S_Q * BW) for
+    2-byte elements (the corrected reading of the review's closed form)."""
+    for (sq, skv, d, n, fl, bw) in [(3128, 2_000_000, 4096, 16, 312e12, 25e9),
+                                    (2048, 1_048_576, 4096, 8, 2.5e15, 153e9),
+                                    (512, 400_000, 1024, 4, 1e14, 1e10)]:
+        c, t = orc.schedule_model(sq, skv, d, n, fl, bw, elem_bytes=2)
+        assert c == "kv"
+        assert t["round_kv"] == t["compute"] > t["comm_kv"]
+        assert t["round_q"] == t["comm_q"] > t["compute"]
+        speedup = t["round_q"] / t["round_kv"]
+        assert abs(speedup / (n * fl / (sq * bw)) - 1) < 1e-12
+
+
+def test_schedule_model_choices(orc):
+    # long visual input: KV stays put
+    assert orc.schedule_model(5514, 15279944, 4096, 16, 312e12, 25e9)[0] == "kv"
+    # S_Q = S_KV, communication-bound: LV-XAttn sends S/n more elements
+    c, t = orc.schedule_model(65536, 65536, 4096, 16, 1e18, 1e9)
+    assert c == "q" and t["comm_kv"] > t["comm_q"]
+    # far more queries than keys: Ring moves the smaller blocks
+    assert orc.schedule_model(1_000_000, 4096, 4096, 8, 312e12, 25e9)[0] == "q"
+    # both compute-bound: equal rounds, the tie goes to LV-XAttn
+    c, t = orc.schedule_model(8192, 8192, 4096, 2, 1e9, 1e18)
+    assert c == "kv" and t["round_kv"] == t["round_q"] == t["compute"]
+    # compute of one round: two contractions of an (S_Q/n x d) block with an
+    # (S_KV/n x d) block, a multiply-add counted as two (brute count below)
+    sq, skv, d, n = 6, 10, 3, 2
+    madds = sum(1 for _ in range(sq // n) for _ in range(skv // n) for _ in range(d)) * 2
+    _, t = orc.schedule_model(sq, skv, d, n, 1.0, 1.0)
+    assert t["compute"] == 2 * madds

@@ -37,6 +37,13 @@ MUTANTS = {
     "bwd_dv_uses_ds": ("gv[d] += P * ld(dout, dt_do, (qb + i) * D + d);",
                        "gv[d] += dS * ld(dout, dt_do, (qb + i) * D + d);"),
     "proj_transposed_weight": ("ld(w_t, dt, nn * E + e)", "ld(w_t, dt, e * HD + nn)"),
+    "model_no_stats_term": ("double lv_elems = 2.0 * S_Q * d / n + S_Q / n;",
+                            "double lv_elems = 2.0 * S_Q * d / n;"),
+    "model_one_contraction": ("double f = 2.0 * (2.0 * q_block * kv_block * d);",
+                              "double f = 2.0 * q_block * kv_block * d;"),
+    "model_ring_sends_q": ("double ring_elems = 2.0 * S_KV * d / n;",
+                           "double ring_elems = 2.0 * S_Q * d / n;"),
+    "model_tie_to_ring": ("return out[3] <= out[4] ? 0 : 1;", "return out[3] < out[4] ? 0 : 1;"),
 }
 
 
@@ -63,6 +70,9 @@ def all_pins(orc):
         lambda: pins.test_backward_finite_differences(orc),
         lambda: pins.test_backward_identities(orc),
         lambda: pins.test_projection_vs_numpy(orc),
+        lambda: pins.test_schedule_model_comm_volume_video_mme(orc),
+        lambda: pins.test_schedule_model_speedup_closed_form(orc),
+        lambda: pins.test_schedule_model_choices(orc),
     ]
     return calls
 
