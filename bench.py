@@ -157,7 +157,7 @@ def main():
     ap.add_argument("--workload", default="lvx_2k_128k")
     ap.add_argument("--mode", default="split", choices=["rounds", "fused", "split"])
     ap.add_argument("--sched", default="kv", choices=["kv", "q"])
-    ap.add_argument("--cpu-rows-per-head", type=int, default=96)
+    ap.add_argument("--cpu-rows-per-head", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy one 1 GiB buffer (a plain copy kernel of "

@@ -31,7 +31,7 @@
  *   - Layout: a bwa_tensor is [B, H, S, D] with element strides sB, sH, sS
  *     and unit stride along D (so [B, S, H, D] storage works by strides).
  *     The base pointer must be 16-byte aligned and sB, sH, sS multiples of
- *     16 bytes.  D must be 64 or 128.
+ *     16 bytes; a row (sS) spans less than 16 MiB.  D must be 64 or 128.
  *   - scale is the softmax scale (callers pass 1/sqrt(D)); it must be finite
  *     and positive.  LSE values are fp32, natural log, scale included.
  *     An empty set of visible keys gives (O = 0, LSE = -inf).

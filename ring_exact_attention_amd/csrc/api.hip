@@ -69,6 +69,8 @@ bwa_status check_tensor(const bwa_tensor* t, const char* name, bool allow_empty_
   if ((uintptr_t)t->ptr % 16 != 0 || (t->sB * es) % 16 != 0 || (t->sH * es) % 16 != 0 ||
       (t->sS * es) % 16 != 0)
     return fail(BWA_ERR_UNSUPPORTED, "%s: base and strides must be 16-byte aligned", name);
+  if (t->sS * es >= ((int64_t)1 << 24))
+    return fail(BWA_ERR_UNSUPPORTED, "%s: row stride of 16 MiB or more", name);
   return BWA_OK;
 }
 

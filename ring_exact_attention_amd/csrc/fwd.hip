@@ -178,25 +178,32 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
   const int64_t sstr = groupB ? p.svS : p.skS;
   const int soff = groupB ? C::K_TILE : 0;
   const int srs = groupB ? VS : KS;
-  auto load_tile = [&](const TileIter& t) {
+  // This thread's chunks are rows srow0 + i * srstep of a tile, 16 bytes at
+  // column chunk scol8.  Their byte offsets from the tile's first row fit in
+  // 24-bit products (row strides are below 16 MiB, checked on the host), so a
+  // tile is loaded from one uniform base plus cheap per-thread offsets.
+  const int srow0 = gtid / (D / 8), scol8 = gtid % (D / 8);
+  constexpr int srstep = C::GT / (D / 8);
+  const uint32_t sstr2 = (uint32_t)(sstr * 2);  // row stride in bytes, < 2^24
+  // Load the tile of `lim` keys (1..BN) starting at row0 of the staged tensor,
+  // branch-free: rows at or past lim repeat the last key (their scores are
+  // masked, their P is zero and the repeated V row is finite).
+  auto load_rows = [&](const bf16* row0, int lim) {
+    const char* base = (const char*)row0;
 #pragma unroll
     for (int i = 0; i < C::KC; ++i) {
-      const int cc = gtid + i * C::GT;
-      const int row = cc / (D / 8), col8 = cc % (D / 8);
-      // rows past the end of the range repeat the last key: their scores are
-      // masked and their P is zero, and the repeated V row is finite
-      const int64_t key = t.kt + row < t.ke ? t.kt + row : t.ke - 1;
-      stg[i] = *(const u32x4*)(ssrc + key * sstr + col8 * 8);
+      const int r = min(srow0 + i * srstep, lim - 1);
+      stg[i] = *(const u32x4*)(base + __umul24((uint32_t)r, sstr2) + scol8 * 16);
     }
+  };
+  auto load_tile = [&](const TileIter& t) {
+    load_rows(ssrc + t.kt * sstr, (int)min(t.ke - t.kt, (int64_t)BN));
   };
   auto store_tile = [&](int buf) {
     bf16* dst = smem + buf * C::STAGE + soff;
 #pragma unroll
-    for (int i = 0; i < C::KC; ++i) {
-      const int cc = gtid + i * C::GT;
-      const int row = cc / (D / 8), col8 = cc % (D / 8);
-      *(u32x4*)(dst + row * srs + col8 * 8) = stg[i];
-    }
+    for (int i = 0; i < C::KC; ++i)
+      *(u32x4*)(dst + (srow0 + i * srstep) * srs + scol8 * 8) = stg[i];
   };
 
   f32x16 sacc[BN / 32];

@@ -83,6 +83,8 @@ def test_ring_fwd_validation(L):
     expect(L, ring_fwd(L, q, k, k, o, mode=7), E.BWA_ERR_INVALID_ARG, "mode")
     expect(L, ring_fwd(L, q, k, k, o, lse=None), E.BWA_ERR_INVALID_ARG, "lse")
     expect(L, ring_fwd(L, q, T(H=3, S=256), T(H=3, S=256), o), E.BWA_ERR_INVALID_ARG, "head")
+    big = T(S=256, strides=(2 * (1 << 23), 1 << 23, 1 << 23))  # 16 MiB rows (bf16)
+    expect(L, ring_fwd(L, q, big, k, o), E.BWA_ERR_UNSUPPORTED, "row stride")
 
 
 def test_ring_fwd_workspace_checks(L):
