@@ -159,6 +159,9 @@ def main():
     ap.add_argument("--sched", default="kv", choices=["kv", "q"])
     ap.add_argument("--cpu-rows-per-head", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--weight-grads", action="store_true",
+                    help="recompute workload: also run the gradients through the projection "
+                         "(dW_k, dW_v, dy) in every step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy one 1 GiB buffer (a plain copy kernel of "
                          "known size, to calibrate HBM byte counters taken under a profiler)")
@@ -175,7 +178,8 @@ def main():
         print(summarize_traffic(*args.summarize_traffic, args.mode, args.profiled_command))
         return
     if args.summarize_stats:
-        print(summarize_stats(args.summarize_stats, args.workload, args.profiled_command))
+        name = args.workload + ("_weight_grads" if args.weight_grads else "")
+        print(summarize_stats(args.summarize_stats, name, args.profiled_command))
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -210,6 +214,10 @@ def main():
         bmode = "rounds" if args.mode == "rounds" else "fused"
         bws = torch.empty(max(bwa.ring_bwd_workspace(q, k, w.n, bmode), 1), dtype=torch.uint8,
                           device=dev)
+        if args.weight_grads:
+            dwk = torch.empty(w.H * w.D, w.E, dtype=torch.float32, device=dev)
+            dwv = torch.empty_like(dwk)
+            dyf = torch.empty(w.B, w.SKV, w.E, dtype=torch.float32, device=dev)
     else:
         q, k, v = make_qkv(w, device=dev)
     o = torch.empty_like(q)
@@ -230,6 +238,8 @@ def main():
             bwa.bwa_kv_recompute(y, wk, wv, w.H, w.D, k=k, v=v)
             bwa.bwa_ring_bwd(q, k, v, o, lse, do, w.n, args.sched, bmode, causal=w.causal,
                              scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=bws)
+            if args.weight_grads:
+                bwa.bwa_kv_recompute_bwd(y, wk, wv, dk, dv, dwk_t=dwk, dwv_t=dwv, dy=dyf)
         else:
             fwd()
 
@@ -256,6 +266,8 @@ def main():
     if recompute:
         gemm = 2.0 * w.B * w.SKV * w.E * w.H * w.D   # one projection
         flops = flops + 4 * gemm + 2.5 * flops      # fwd + 2x(K, V) recompute + bwd (10 S_Q S_KV D)
+        if args.weight_grads:
+            flops += 4 * gemm                       # dW_k, dW_v, and dy through both projections
     tflops = flops / (ms * 1e-3) / 1e12
     # compulsory HBM bytes of the forward: read Q, K, V once, write O and LSE
     esz = 2 if w.dtype == "bf16" else 4
@@ -272,6 +284,8 @@ def main():
                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                     "traffic": None, "kernel": "whole step (gemm_kv, fwd, bwd kernels)",
                     "launches_per_step": None}
+        if args.weight_grads:
+            roofline["kernel"] = "whole step (gemm_kv, fwd, bwd, gemm_dw, gemm_dy kernels)"
     else:
         # the forward kernel's share of the step: in split mode the merge kernel is
         # the rest; its duration is measured separately below
@@ -301,7 +315,8 @@ def main():
 
     out = {
         "metric": METRIC if args.workload == "lvx_2k_128k" else
-        f"{'training-step' if recompute else 'attention'} TFLOP/s, {w.name}, 1 GPU",
+        f"{'training-step' if recompute else 'attention'} TFLOP/s, {w.name}"
+        f"{' with weight gradients' if args.weight_grads else ''}, 1 GPU",
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,

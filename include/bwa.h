@@ -208,6 +208,27 @@ bwa_status bwa_kv_recompute(const void* y, const void* wk_t, const void* wv_t, i
                             const bwa_tensor* k, const bwa_tensor* v, void* stream);
 
 /*
+ * Gradients through the K/V recompute (same passage as bwa_kv_recompute: the
+ * backward of K = y W_k, V = y W_v from the one shared y):
+ *   dwk_t[n, e] = sum_{b,s} dk[b, h, s, d] * y[b, s, e]    (n = h*D + d),
+ *   dwv_t likewise with dv,
+ *   dy[b, s, e] = sum_n dk[b, h, s, d] * wk_t[n, e] + dv[b, h, s, d] * wv_t[n, e].
+ *   y, wk_t, wv_t as in bwa_kv_recompute (bf16, contiguous).
+ *   dk, dv  bf16 [B, H, S_KV, D] tensors sharing one set of strides.
+ *   dwk_t, dwv_t  fp32 [H*D, E] contiguous (gradients of wk_t, wv_t);
+ *   dy      fp32 [B, S_KV, E] contiguous.  Any output may be NULL (skipped),
+ *           not all three.
+ *   accumulate = 0 overwrites the outputs, 1 adds to them (for cross-attention
+ *   layers that share y).
+ * E and H*D must be multiples of 256, S_KV a multiple of 64.  fp32
+ * accumulation of bf16 products; no other rounding.
+ */
+bwa_status bwa_kv_recompute_bwd(const void* y, const void* wk_t, const void* wv_t,
+                                const bwa_tensor* dk, const bwa_tensor* dv, int64_t B,
+                                int64_t S_KV, int64_t E, int64_t H, int64_t D, float* dwk_t,
+                                float* dwv_t, float* dy, int32_t accumulate, void* stream);
+
+/*
  * Per-round cost model of the two ring schedules and the choice between them
  * (LV-XAttn review, "What carries the argument": the per-round runtime
  * identity).  With d = H*D the model width, a round of either schedule

@@ -73,6 +73,9 @@ def _load():
         lib.orc_attn_bwd_heads.argtypes = [vp, vp, vp, vp, ci, ci, i64, i64, i64, i64, i64, f64,
                                            ci, vp, i64, vp, i64, vp, vp, vp, vp, vp]
         lib.orc_kv_proj_rows.argtypes = [vp, vp, ci, i64, i64, i64, i64, vp, i64, vp]
+        lib.orc_kv_grad_w_rows.argtypes = [vp, vp, ci, i64, i64, i64, i64, i64, vp, i64, vp]
+        lib.orc_kv_grad_y_rows.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, i64, i64, vp, i64,
+                                           vp]
         lib.orc_schedule_model.argtypes = [f64] * 7 + [vp]
         lib.orc_schedule_model.restype = ci
         _lib = lib
@@ -278,3 +281,46 @@ def schedule_model(S_Q, S_KV, d, n, flops_per_s, bytes_per_s, elem_bytes=2):
                                    out.ctypes.data)
     keys = ("compute", "comm_kv", "comm_q", "round_kv", "round_q")
     return ("kv" if c == 0 else "q"), dict(zip(keys, out.tolist()))
+
+
+def _rows_arg(rows):
+    if rows is None:
+        return None, -1, None
+    keep = np.ascontiguousarray(np.asarray(rows, np.int64))
+    return keep.ctypes.data, keep.size, keep
+
+
+def kv_grad_w(y, g, rows=None):
+    """dW_t[n, e] = sum_{b,s} g[b,h,s,d] y[b,s,e] (n = h*D + d): the gradient of
+    w_t ([H*D, E]) for K = y W, W = w_t^T, given dK = g [B,H,S,D].  rows selects
+    rows n; returns [len(rows) or H*D, E]."""
+    B, S, E = y.shape
+    _, H, S2, D = g.shape
+    if S2 != S or g.shape[0] != B:
+        raise ValueError("g must be [B, H, S, D] matching y [B, S, E]")
+    py, dy_, ky = _arr(y)
+    pg, dg, kg = _arr(g)
+    if dy_ != dg:
+        raise ValueError("y and g must share a dtype")
+    pr, nr, keep = _rows_arg(rows)
+    out = np.zeros((H * D if nr < 0 else nr, E), np.float64)
+    _load().orc_kv_grad_w_rows(py, pg, dg, B, S, E, H, D, pr, nr, out.ctypes.data)
+    del ky, kg, keep
+    return out
+
+
+def kv_grad_y(gk, gv, wk_t, wv_t, rows=None):
+    """dy[b, s, e] = sum_n gk[b,h,s,d] wk_t[n,e] + gv[b,h,s,d] wv_t[n,e]: the
+    gradient of y through both projections.  rows selects flat rows b*S + s;
+    returns [len(rows) or B*S, E]."""
+    B, H, S, D = gk.shape
+    E = wk_t.shape[1]
+    ptrs = [_arr(t) for t in (gk, gv, wk_t, wv_t)]
+    if len({p[1] for p in ptrs}) != 1:
+        raise ValueError("inputs must share a dtype")
+    pr, nr, keep = _rows_arg(rows)
+    out = np.zeros((B * S if nr < 0 else nr, E), np.float64)
+    _load().orc_kv_grad_y_rows(ptrs[0][0], ptrs[1][0], ptrs[2][0], ptrs[3][0], ptrs[0][1], B, S, E,
+                               H, D, pr, nr, out.ctypes.data)
+    del ptrs, keep
+    return out

@@ -337,6 +337,56 @@ void orc_kv_proj_rows(const void* y, const void* w_t, int dt, int64_t B, int64_t
 }
 
 /* ------------------------------------------------------------------------
+ * Gradients through the recompute ([LVX] "What carries the argument": K, V
+ * are recomputed from the one shared y, so the backward also yields the
+ * gradients of W_k, W_v and y).  Plain definitions of the derivatives of
+ * K[b,h,s,d] = sum_e y[b,s,e] * w_t[h*D+d, e]:
+ *   dW_t[n, e] = sum_{b,s} g[b, h, s, d] * y[b, s, e]       (n = h*D + d)
+ *   dy[b, s, e] = sum_n gk[b, h, s, d] * wk_t[n, e] + gv[b, h, s, d] * wv_t[n, e]
+ * g, gk, gv are [B, H, S, D] contiguous. */
+static double g_at(const void* g, int dt, int64_t H, int64_t S, int64_t D, int64_t b, int64_t s,
+                   int64_t n) {
+  int64_t h = n / D, d = n % D;
+  return ld(g, dt, ((b * H + h) * S + s) * D + d);
+}
+
+/* rows n of dW_t (nrows of them, or all H*D when nrows < 0), out [nrows, E] */
+void orc_kv_grad_w_rows(const void* y, const void* g, int dt, int64_t B, int64_t S, int64_t E,
+                        int64_t H, int64_t D, const int64_t* rows, int64_t nrows, double* out) {
+  int64_t cnt = nrows < 0 ? H * D : nrows;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t t = 0; t < cnt; ++t) {
+    int64_t n = nrows < 0 ? t : rows[t];
+    for (int64_t e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int64_t b = 0; b < B; ++b)
+        for (int64_t s = 0; s < S; ++s)
+          acc += g_at(g, dt, H, S, D, b, s, n) * ld(y, dt, (b * S + s) * E + e);
+      out[t * E + e] = acc;
+    }
+  }
+}
+
+/* rows (b*S + s) of dy (nrows of them, or all B*S when nrows < 0), out [nrows, E] */
+void orc_kv_grad_y_rows(const void* gk, const void* gv, const void* wk_t, const void* wv_t,
+                        int dt, int64_t B, int64_t S, int64_t E, int64_t H, int64_t D,
+                        const int64_t* rows, int64_t nrows, double* out) {
+  int64_t cnt = nrows < 0 ? B * S : nrows;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t t = 0; t < cnt; ++t) {
+    int64_t row = nrows < 0 ? t : rows[t];
+    int64_t b = row / S, s = row % S;
+    for (int64_t e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int64_t n = 0; n < H * D; ++n)
+        acc += g_at(gk, dt, H, S, D, b, s, n) * ld(wk_t, dt, n * E + e) +
+               g_at(gv, dt, H, S, D, b, s, n) * ld(wv_t, dt, n * E + e);
+      out[t * E + e] = acc;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------
  * Per-round cost model of the two ring schedules ([LVX] "What carries the
  * argument": a round lasts max(f(S_Q d/n, S_KV d/n), comm(message)), with
  * message 2 S_Q d/n + S_Q/n elements for LV-XAttn (Q_i, O_i, L_i) and

@@ -13,6 +13,7 @@ from ._bwa import (  # noqa: F401
     SCHED_Q_STATIONARY,
     bwa_choose_schedule,
     bwa_kv_recompute,
+    bwa_kv_recompute_bwd,
     bwa_merge,
     bwa_merge_partials,
     bwa_partial_fwd,
@@ -24,5 +25,5 @@ from ._bwa import (  # noqa: F401
 )
 
 __all__ = ["bwa_partial_fwd", "bwa_merge", "bwa_merge_partials", "bwa_ring_fwd", "bwa_ring_bwd",
-           "bwa_kv_recompute", "bwa_choose_schedule",
+           "bwa_kv_recompute", "bwa_kv_recompute_bwd", "bwa_choose_schedule",
            "BwaError", "lib"]

@@ -28,7 +28,8 @@ MODES = {"rounds": MODE_ROUNDS, "fused": MODE_FUSED, "split": MODE_SPLIT}
 
 EXPORTED = ("bwa_partial_fwd", "bwa_merge", "bwa_merge_partials", "bwa_ring_fwd_workspace",
             "bwa_ring_fwd",
-            "bwa_ring_bwd_workspace", "bwa_ring_bwd", "bwa_kv_recompute", "bwa_choose_schedule",
+            "bwa_ring_bwd_workspace", "bwa_ring_bwd", "bwa_kv_recompute", "bwa_kv_recompute_bwd",
+            "bwa_choose_schedule",
             "bwa_status_string",
             "bwa_last_error", "bwa_version")
 
@@ -81,6 +82,8 @@ def lib():
         for name in ("bwa_partial_fwd", "bwa_merge", "bwa_merge_partials", "bwa_ring_fwd",
                      "bwa_ring_bwd", "bwa_kv_recompute"):
             getattr(L, name).restype = ci
+        L.bwa_kv_recompute_bwd.argtypes = [vp, vp, vp, T, T, i64, i64, i64, i64, i64, vp, vp, vp,
+                                           ctypes.c_int32, vp]
         L.bwa_choose_schedule.argtypes = [i64, i64, i64, ctypes.c_int32, ctypes.c_double,
                                           ctypes.c_double, ctypes.c_int32,
                                           ctypes.POINTER(ctypes.c_int32),
@@ -286,3 +289,34 @@ def bwa_choose_schedule(S_Q, S_KV, d_model, n, flops_per_s, bytes_per_s, elem_by
                                  elem_bytes, ctypes.byref(choice), ctypes.byref(m)))
     times = {f: getattr(m, f) for f, _ in ScheduleModel._fields_}
     return ("kv" if choice.value == SCHED_KV_STATIONARY else "q"), times
+
+
+def bwa_kv_recompute_bwd(y, wk_t, wv_t, dk, dv, dwk_t=None, dwv_t=None, dy=None,
+                         accumulate=False, outputs=("dwk_t", "dwv_t", "dy")):
+    """Gradients of K = y W_k, V = y W_v: (dwk_t [H*D, E], dwv_t, dy [B, S, E]), fp32.
+    Outputs not passed are allocated (only those named in `outputs`)."""
+    for name, t in (("y", y), ("wk_t", wk_t), ("wv_t", wv_t)):
+        _on_device(t)
+        if not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a contiguous bf16 tensor")
+    B, S, E = y.shape
+    H, D = dk.shape[1], dk.shape[3]
+    dev = y.device
+    if dwk_t is None and "dwk_t" in outputs:
+        dwk_t = torch.zeros(H * D, E, dtype=torch.float32, device=dev)
+    if dwv_t is None and "dwv_t" in outputs:
+        dwv_t = torch.zeros(H * D, E, dtype=torch.float32, device=dev)
+    if dy is None and "dy" in outputs:
+        dy = torch.zeros(B, S, E, dtype=torch.float32, device=dev)
+    for name, t in (("dwk_t", dwk_t), ("dwv_t", dwv_t), ("dy", dy)):
+        if t is not None and (not t.is_contiguous() or t.dtype != torch.float32):
+            raise ValueError(f"{name} must be a contiguous fp32 tensor")
+    L = lib()
+    ka, va = as_bwa(dk), as_bwa(dv)
+    _check(L.bwa_kv_recompute_bwd(_ptr(y), _ptr(wk_t), _ptr(wv_t), ctypes.byref(ka),
+                                  ctypes.byref(va), B, S, E, H, D,
+                                  _ptr(dwk_t) if dwk_t is not None else None,
+                                  _ptr(dwv_t) if dwv_t is not None else None,
+                                  _ptr(dy) if dy is not None else None, 1 if accumulate else 0,
+                                  _stream(dev)))
+    return dwk_t, dwv_t, dy

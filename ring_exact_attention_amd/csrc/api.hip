@@ -20,6 +20,10 @@ hipError_t finalize_launch(FwdParams p, int dtype_bf16, hipStream_t st);
 bool bwd_supported(int dtype, int D);
 size_t bwd_workspace_bytes(int64_t BH, int64_t SQ, int64_t SKV, int D, int n, int mode);
 hipError_t bwd_run(const BwdArgs& a, hipStream_t st);
+hipError_t gemm_grad_launch(const void* y, const void* wk_t, const void* wv_t,
+                            const bwa_tensor* dk, const bwa_tensor* dv, int64_t B, int64_t S,
+                            int64_t E, int64_t H, int64_t Dh, float* dwk_t, float* dwv_t,
+                            float* dy, int accumulate, hipStream_t st);
 hipError_t gemm_kv_launch(const void* y, const void* wk_t, const void* wv_t, int64_t B, int64_t S,
                           int64_t E, int64_t H, int64_t D, const bwa_tensor* k,
                           const bwa_tensor* v, hipStream_t st);
@@ -401,6 +405,37 @@ bwa_status bwa_kv_recompute(const void* y, const void* wk_t, const void* wv_t, i
     return fail(BWA_ERR_UNSUPPORTED, "y, wk_t, wv_t must be 16-byte aligned");
   hipError_t e = bwa::gemm_kv_launch(y, wk_t, wv_t, B, S_KV, E, H, D, k, v, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kv recompute launch");
+  return BWA_OK;
+}
+
+bwa_status bwa_kv_recompute_bwd(const void* y, const void* wk_t, const void* wv_t,
+                                const bwa_tensor* dk, const bwa_tensor* dv, int64_t B,
+                                int64_t S_KV, int64_t E, int64_t H, int64_t D, float* dwk_t,
+                                float* dwv_t, float* dy, int32_t accumulate, void* stream) {
+  if (B <= 0 || S_KV <= 0 || E <= 0 || H <= 0) return fail(BWA_ERR_INVALID_ARG, "bad sizes");
+  if (D != 64 && D != 128) return fail(BWA_ERR_UNSUPPORTED, "D must be 64 or 128");
+  if (E % 256 != 0) return fail(BWA_ERR_UNSUPPORTED, "E must be a multiple of 256");
+  if ((H * D) % 256 != 0) return fail(BWA_ERR_UNSUPPORTED, "H*D must be a multiple of 256");
+  if (S_KV % 64 != 0) return fail(BWA_ERR_UNSUPPORTED, "S_KV must be a multiple of 64");
+  if (B * S_KV >= kMaxDim || E >= kMaxDim || H * D >= kMaxDim)
+    return fail(BWA_ERR_UNSUPPORTED, "sizes too large");
+  bwa_status s;
+  if ((s = check_tensor(dk, "dk", false)) != BWA_OK) return s;
+  if ((s = check_tensor(dv, "dv", false)) != BWA_OK) return s;
+  if (dk->dtype != BWA_BF16 || dv->dtype != BWA_BF16 || dk->B != B || dv->B != B ||
+      dk->H != H || dv->H != H || dk->S != S_KV || dv->S != S_KV || dk->D != D || dv->D != D)
+    return fail(BWA_ERR_INVALID_ARG, "dk / dv shape or dtype does not match [B, H, S_KV, D] bf16");
+  if (dk->sB != dv->sB || dk->sH != dv->sH || dk->sS != dv->sS)
+    return fail(BWA_ERR_UNSUPPORTED, "dk and dv must share one layout (equal strides)");
+  if (!dwk_t && !dwv_t && !dy) return fail(BWA_ERR_INVALID_ARG, "no output requested");
+  if (!y || !wk_t || !wv_t) return fail(BWA_ERR_INVALID_ARG, "NULL input pointer");
+  if ((uintptr_t)y % 16 || (uintptr_t)wk_t % 16 || (uintptr_t)wv_t % 16)
+    return fail(BWA_ERR_UNSUPPORTED, "y, wk_t, wv_t must be 16-byte aligned");
+  if ((uintptr_t)dwk_t % 4 || (uintptr_t)dwv_t % 4 || (uintptr_t)dy % 4)
+    return fail(BWA_ERR_UNSUPPORTED, "outputs must be 4-byte aligned");
+  hipError_t e = bwa::gemm_grad_launch(y, wk_t, wv_t, dk, dv, B, S_KV, E, H, D, dwk_t, dwv_t, dy,
+                                       accumulate ? 1 : 0, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kv recompute backward launch");
   return BWA_OK;
 }
 

@@ -210,3 +210,21 @@ def test_choose_schedule_validation(L):
         assert f(*args, ctypes.byref(choice), None) == _bwa.BWA_ERR_INVALID_ARG, args
     assert f(10, 10, 8, 2, 1e12, 1e9, 2, None, None) == _bwa.BWA_ERR_INVALID_ARG
     assert f(10, 10, 8, 2, 1e12, 1e9, 2, ctypes.byref(choice), None) == _bwa.BWA_OK
+
+
+def test_kv_recompute_bwd_validation(L):
+    f = L.bwa_kv_recompute_bwd
+    E = _bwa
+    g = T(B=1, H=2, S=128, D=128)
+    F = ctypes.c_void_p(FAKE)
+
+    def call(B=1, S=128, Esz=256, H=2, D=128, dk=g, dv=g, outs=(F, F, F)):
+        return f(F, F, F, ctypes.byref(dk), ctypes.byref(dv), B, S, Esz, H, D, *outs, 0, None)
+    expect(L, call(Esz=192), E.BWA_ERR_UNSUPPORTED, "multiple of 256")
+    expect(L, call(S=100, dk=T(S=100), dv=T(S=100)), E.BWA_ERR_UNSUPPORTED, "multiple of 64")
+    expect(L, call(H=1, dk=T(H=1, S=128), dv=T(H=1, S=128)), E.BWA_ERR_UNSUPPORTED,
+           "H*D must be a multiple of 256")
+    expect(L, call(dv=T(S=128, strides=(2 * 128 * 128, 128, 2 * 128))), E.BWA_ERR_UNSUPPORTED,
+           "share one layout")
+    expect(L, call(outs=(None, None, None)), E.BWA_ERR_INVALID_ARG, "no output")
+    expect(L, call(dk=T(S=64)), E.BWA_ERR_INVALID_ARG, "does not match")

@@ -145,3 +145,85 @@ def test_full_recompute_bwd(bwa, orc):
     check_grad(dq[0, heads], ref["dq"], "dq full")
     check_grad(dk[0, heads][:, kk], ref["dk"], "dk full (sampled keys)")
     check_grad(dv[0, heads][:, kk], ref["dv"], "dv full (sampled keys)")
+
+
+# ---------------------------------------------------------------- gradients through the recompute
+
+def _check_rows(got, ref, what, rel=2e-5):
+    """fp32 accumulation of exact bf16 products: every element within `rel` of
+    the largest reference magnitude of its row block."""
+    got = np.asarray(got, np.float64)
+    err = np.abs(got - ref).max()
+    scale = np.abs(ref).max()
+    assert err <= rel * scale, f"{what}: max err {err:.3e} vs max |ref| {scale:.3e}"
+    assert np.linalg.norm(got - ref) <= rel * np.linalg.norm(ref), what
+
+
+@pytest.mark.parametrize("shape", [(1, 64, 256, 2, 128), (2, 128, 256, 4, 64),
+                                   (1, 320, 512, 2, 128)], ids=lambda s: "x".join(map(str, s)))
+def test_kv_recompute_bwd_small(bwa, orc, shape):
+    B, S, E, H, D = shape
+    g = torch.Generator().manual_seed(S + E)
+    y = (torch.randn(B, S, E, generator=g) * 0.5).bfloat16()
+    wk = (torch.randn(H * D, E, generator=g) * 0.1).bfloat16()
+    wv = (torch.randn(H * D, E, generator=g) * 0.1).bfloat16()
+    gk = torch.randn(B, H, S, D, generator=g).bfloat16()
+    gv = torch.randn(B, H, S, D, generator=g).bfloat16()
+    log_case(recompute_bwd=shape)
+    dwk, dwv, dy = bwa.bwa_kv_recompute_bwd(y.cuda(), wk.cuda(), wv.cuda(), gk.cuda(), gv.cuda())
+    torch.cuda.synchronize()
+    _check_rows(dwk.cpu().numpy(), orc.kv_grad_w(y, gk), "dW_k")
+    _check_rows(dwv.cpu().numpy(), orc.kv_grad_w(y, gv), "dW_v")
+    _check_rows(dy.cpu().numpy().reshape(B * S, E), orc.kv_grad_y(gk, gv, wk, wv), "dy")
+
+
+def test_kv_recompute_bwd_accumulate_strided_and_partial_outputs(bwa, orc):
+    B, S, E, H, D = 1, 128, 256, 2, 128
+    g = torch.Generator().manual_seed(77)
+    y = (torch.randn(B, S, E, generator=g) * 0.5).bfloat16().cuda()
+    wk = (torch.randn(H * D, E, generator=g) * 0.1).bfloat16().cuda()
+    wv = (torch.randn(H * D, E, generator=g) * 0.1).bfloat16().cuda()
+    # dK, dV stored [B, S, H, D] and passed as [B, H, S, D] views (equal strides)
+    gk = torch.randn(B, S, H, D, generator=g).bfloat16().cuda().transpose(1, 2)
+    gv = torch.randn(B, S, H, D, generator=g).bfloat16().cuda().transpose(1, 2)
+    log_case(recompute_bwd="strided+accumulate")
+    ref_w = orc.kv_grad_w(y.cpu(), gk.cpu().contiguous())
+    ref_y = orc.kv_grad_y(gk.cpu().contiguous(), gv.cpu().contiguous(), wk.cpu(), wv.cpu())
+    dwk = torch.full((H * D, E), 0.25, device="cuda")
+    dy = torch.full((B, S, E), -0.5, device="cuda")
+    bwa.bwa_kv_recompute_bwd(y, wk, wv, gk, gv, dwk_t=dwk, dy=dy, accumulate=True,
+                             outputs=("dwk_t", "dy"))
+    bwa.bwa_kv_recompute_bwd(y, wk, wv, gk, gv, dwk_t=dwk, dy=dy, accumulate=True,
+                             outputs=("dwk_t", "dy"))
+    torch.cuda.synchronize()
+    _check_rows(dwk.cpu().numpy() - 0.25, 2 * ref_w, "dW_k accumulated twice")
+    _check_rows(dy.cpu().numpy().reshape(B * S, E) + 0.5, 2 * ref_y, "dy accumulated twice")
+    only_dy = bwa.bwa_kv_recompute_bwd(y, wk, wv, gk, gv, outputs=("dy",))
+    torch.cuda.synchronize()
+    assert only_dy[0] is None and only_dy[1] is None
+    _check_rows(only_dy[2].cpu().numpy().reshape(B * S, E), ref_y, "dy alone")
+
+
+def test_kv_recompute_bwd_full_size_sampled(bwa, orc):
+    """Recompute workload sizes (y [1, 65536, 4096], W [4096, 4096], 32 heads of
+    128): sampled rows of dW_k, dW_v (each a 65536-term sum) and of dy."""
+    from ring_exact_attention_amd.inputs import WORKLOADS, make_recompute
+    w = WORKLOADS["recompute_bwd"]
+    log_case(workload=w.name, stage="weight and feature gradients")
+    y, wk, wv = make_recompute(w, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(w.seed + 303)
+    gk = torch.randn(w.B, w.H, w.SKV, w.D, generator=g, device="cuda").bfloat16()
+    gv = torch.randn(w.B, w.H, w.SKV, w.D, generator=g, device="cuda").bfloat16()
+    dwk, dwv, dy = bwa.bwa_kv_recompute_bwd(y, wk, wv, gk, gv)
+    torch.cuda.synchronize()
+    for x in (dwk, dwv, dy):
+        assert torch.isfinite(x).all()
+    yc, gkc, gvc = y.cpu(), gk.cpu(), gv.cpu()
+    nrows = [0, 1234, w.H * w.D - 1]
+    log_case(workload=w.name, stage="oracle dW rows")
+    _check_rows(dwk[nrows].cpu().numpy(), orc.kv_grad_w(yc, gkc, rows=nrows), "dW_k rows", 1e-4)
+    _check_rows(dwv[nrows].cpu().numpy(), orc.kv_grad_w(yc, gvc, rows=nrows), "dW_v rows", 1e-4)
+    srows = [0, 40000, w.B * w.SKV - 1]
+    log_case(workload=w.name, stage="oracle dy rows")
+    ref = orc.kv_grad_y(gkc, gvc, wk.cpu(), wv.cpu(), rows=srows)
+    _check_rows(dy.reshape(-1, w.E)[srows].cpu().numpy(), ref, "dy rows", 1e-4)

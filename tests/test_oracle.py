@@ -481,3 +481,47 @@ def test_schedule_model_choices(orc):
     madds = sum(1 for _ in range(sq // n) for _ in range(skv // n) for _ in range(d)) * 2
     _, t = orc.schedule_model(sq, skv, d, n, 1.0, 1.0)
     assert t["compute"] == 2 * madds
+
+
+# ---------------------------------------------------------------- gradients through the recompute
+
+def _flat_heads(g):
+    B, H, S, D = g.shape
+    return g.transpose(0, 2, 1, 3).reshape(B * S, H * D)  # column n = h*D + d
+
+
+def test_recompute_grads_vs_numpy(orc):
+    B, S, E, H, D = 2, 5, 12, 3, 4
+    y = rnd((B, S, E), 160)
+    wk, wv = rnd((H * D, E), 161), rnd((H * D, E), 162)
+    gk, gv = rnd((B, H, S, D), 163), rnd((B, H, S, D), 164)
+    dW = orc.kv_grad_w(y, gk)
+    np.testing.assert_allclose(dW, _flat_heads(gk).T @ y.reshape(B * S, E), rtol=1e-12,
+                               atol=1e-13)
+    dy = orc.kv_grad_y(gk, gv, wk, wv)
+    np.testing.assert_allclose(dy, _flat_heads(gk) @ wk + _flat_heads(gv) @ wv, rtol=1e-12,
+                               atol=1e-13)
+    np.testing.assert_array_equal(orc.kv_grad_w(y, gk, rows=[7, 0, 11]), dW[[7, 0, 11]])
+    np.testing.assert_array_equal(orc.kv_grad_y(gk, gv, wk, wv, rows=[9, 2]), dy[[9, 2]])
+
+
+def test_recompute_grads_are_adjoints(orc):
+    """The gradients are the adjoints of the projection (pinned against numpy
+    above and in test_projection_vs_numpy): for any Y and W,
+    <g, proj(Y, w)> = <dy(g), Y> and <g, proj(y, W)> = <dW(y, g), W>."""
+    B, S, E, H, D = 1, 6, 8, 2, 4
+    y, Y = rnd((B, S, E), 170), rnd((B, S, E), 171)
+    w, W = rnd((H * D, E), 172), rnd((H * D, E), 173)
+    g = rnd((B, H, S, D), 174)
+    zero_g, zero_w = np.zeros_like(g), np.zeros_like(w)
+    lhs = float(np.sum(g * orc.kv_proj(Y, w, H, D)))
+    rhs = float(np.sum(orc.kv_grad_y(g, zero_g, w, zero_w).reshape(B, S, E) * Y))
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+    lhs = float(np.sum(g * orc.kv_proj(y, W, H, D)))
+    rhs = float(np.sum(orc.kv_grad_w(y, g) * W))
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+    # dy is linear in (gk, gv): the V path contributes through wv alone
+    dy_k = orc.kv_grad_y(g, zero_g, w, W)
+    dy_v = orc.kv_grad_y(zero_g, g, w, W)
+    np.testing.assert_allclose(orc.kv_grad_y(g, g, w, W), dy_k + dy_v, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dy_v, orc.kv_grad_y(g, zero_g, W, w), rtol=0, atol=0)

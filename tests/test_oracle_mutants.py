@@ -44,6 +44,12 @@ MUTANTS = {
     "model_ring_sends_q": ("double ring_elems = 2.0 * S_KV * d / n;",
                            "double ring_elems = 2.0 * S_Q * d / n;"),
     "model_tie_to_ring": ("return out[3] <= out[4] ? 0 : 1;", "return out[3] < out[4] ? 0 : 1;"),
+    "grad_head_index_swapped": ("int64_t h = n / D, d = n % D;", "int64_t d = n / D, h = n % D;"),
+    "grad_y_drops_v": ("acc += g_at(gk, dt, H, S, D, b, s, n) * ld(wk_t, dt, n * E + e) +\n"
+                       "               g_at(gv, dt, H, S, D, b, s, n) * ld(wv_t, dt, n * E + e);",
+                       "acc += g_at(gk, dt, H, S, D, b, s, n) * ld(wk_t, dt, n * E + e);"),
+    "grad_w_y_row_off_by_batch": ("acc += g_at(g, dt, H, S, D, b, s, n) * ld(y, dt, (b * S + s) * E + e);",
+                                  "acc += g_at(g, dt, H, S, D, b, s, n) * ld(y, dt, s * E + e);"),
 }
 
 
@@ -73,6 +79,8 @@ def all_pins(orc):
         lambda: pins.test_schedule_model_comm_volume_video_mme(orc),
         lambda: pins.test_schedule_model_speedup_closed_form(orc),
         lambda: pins.test_schedule_model_choices(orc),
+        lambda: pins.test_recompute_grads_vs_numpy(orc),
+        lambda: pins.test_recompute_grads_are_adjoints(orc),
     ]
     return calls
 
