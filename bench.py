@@ -155,7 +155,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="lvx_2k_128k")
-    ap.add_argument("--mode", default="split", choices=["rounds", "fused", "split"])
+    ap.add_argument("--mode", default="split", choices=["rounds", "fused", "split", "rounds_transfer"])
     ap.add_argument("--sched", default="kv", choices=["kv", "q"])
     ap.add_argument("--cpu-rows-per-head", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -211,7 +211,7 @@ def main():
         v = torch.empty_like(k)
         bwa.bwa_kv_recompute(y, wk, wv, w.H, w.D, k=k, v=v)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        bmode = "rounds" if args.mode == "rounds" else "fused"
+        bmode = "rounds" if args.mode in ("rounds", "rounds_transfer") else "fused"
         bws = torch.empty(max(bwa.ring_bwd_workspace(q, k, w.n, bmode), 1), dtype=torch.uint8,
                           device=dev)
         if args.weight_grads:
@@ -277,7 +277,7 @@ def main():
     # kernel; in rounds mode n launches (one per round) plus a small finalize;
     # in split mode one launch plus the merge.  Per-launch flops are the
     # step's flops divided by the launches of that kernel.
-    launches = w.n if args.mode == "rounds" else 1
+    launches = w.n if args.mode in ("rounds", "rounds_transfer") else 1
     if recompute:
         # several kernels per step (GEMM, forward, backward); report the step as a whole
         roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,

@@ -86,8 +86,20 @@ typedef enum {
  *           schedule order, carrying the softmax state in registers.
  *   SPLIT:  one launch computes every pair's partial into the workspace,
  *           then one merge launch combines them in schedule order.
+ *   ROUNDS_TRANSFER: ROUNDS, plus the exchange made real: after every round
+ *           but the last, each worker's outgoing blocks are copied on the
+ *           device into the receive buffers the next round computes from
+ *           (KV-stationary: Q_i in its dtype, O_i and L_i in fp32; Q-stationary:
+ *           K_i and V_i), so the per-round message bytes are HBM traffic.
+ *           Results are bitwise equal to ROUNDS.  (LV-XAttn review, "What
+ *           carries the argument": the blocks each schedule sends per round.)
  */
-typedef enum { BWA_MODE_ROUNDS = 0, BWA_MODE_FUSED = 1, BWA_MODE_SPLIT = 2 } bwa_mode;
+typedef enum {
+  BWA_MODE_ROUNDS = 0,
+  BWA_MODE_FUSED = 1,
+  BWA_MODE_SPLIT = 2,
+  BWA_MODE_ROUNDS_TRANSFER = 3
+} bwa_mode;
 
 typedef struct bwa_tensor {
   void* ptr;       /* device pointer, 16-byte aligned */

@@ -20,11 +20,12 @@ BWA_OK, BWA_ERR_INVALID_ARG, BWA_ERR_UNSUPPORTED, BWA_ERR_WORKSPACE, BWA_ERR_HIP
     BWA_ERR_INTERNAL = range(6)
 BWA_F32, BWA_BF16 = 0, 1
 SCHED_KV_STATIONARY, SCHED_Q_STATIONARY = 0, 1
-MODE_ROUNDS, MODE_FUSED, MODE_SPLIT = 0, 1, 2
+MODE_ROUNDS, MODE_FUSED, MODE_SPLIT, MODE_ROUNDS_TRANSFER = 0, 1, 2, 3
 
 SCHEDULES = {"kv": SCHED_KV_STATIONARY, "lv": SCHED_KV_STATIONARY, "kv_stationary": 0,
              "q": SCHED_Q_STATIONARY, "ring": SCHED_Q_STATIONARY, "q_stationary": 1}
-MODES = {"rounds": MODE_ROUNDS, "fused": MODE_FUSED, "split": MODE_SPLIT}
+MODES = {"rounds": MODE_ROUNDS, "fused": MODE_FUSED, "split": MODE_SPLIT,
+         "rounds_transfer": MODE_ROUNDS_TRANSFER}
 
 EXPORTED = ("bwa_partial_fwd", "bwa_merge", "bwa_merge_partials", "bwa_ring_fwd_workspace",
             "bwa_ring_fwd",

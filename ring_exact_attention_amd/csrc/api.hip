@@ -17,6 +17,8 @@ hipError_t merge2_launch(int64_t rows, int D, const float* oa, const float* la, 
                          const float* lb, float* oo, float* lo, hipStream_t st);
 hipError_t split_merge_launch(FwdParams p, int dtype_bf16, hipStream_t st);
 hipError_t finalize_launch(FwdParams p, int dtype_bf16, hipStream_t st);
+hipError_t copy_rows_launch(const void* src, int64_t sB, int64_t sH, int64_t sS, void* dst, int B,
+                            int H, int64_t S, int row_bytes, hipStream_t st);
 bool bwd_supported(int dtype, int D);
 size_t bwd_workspace_bytes(int64_t BH, int64_t SQ, int64_t SKV, int D, int n, int mode);
 hipError_t bwd_run(const BwdArgs& a, hipStream_t st);
@@ -110,10 +112,26 @@ bwa_status check_scale(float scale) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t fwd_ws_bytes(int64_t BH, int64_t SQ, int D, int n, int mode) {
+// ROUNDS_TRANSFER workspace: the stationary (O, L) of the Q-stationary
+// schedule, then two receive slots, each large enough for either schedule's
+// rotating blocks: (Q, O, L) or (K, V).
+struct XferLayout {
+  size_t o, l, q, kv, slot;
+  XferLayout(int64_t BH, int64_t SQ, int64_t SKV, int D, size_t es) {
+    o = align256((size_t)(BH * SQ * D) * 4);
+    l = align256((size_t)(BH * SQ) * 4);
+    q = align256((size_t)(BH * SQ * D) * es);
+    kv = align256((size_t)(BH * SKV * D) * es);
+    slot = q + o + l > 2 * kv ? q + o + l : 2 * kv;
+  }
+  size_t total() const { return o + l + 2 * slot; }
+};
+
+size_t fwd_ws_bytes(int64_t BH, int64_t SQ, int64_t SKV, int D, size_t es, int n, int mode) {
   if (mode == BWA_MODE_ROUNDS) return align256((size_t)(BH * SQ * D) * 4);
   if (mode == BWA_MODE_SPLIT)
     return align256((size_t)n * BH * SQ * D * 4) + align256((size_t)n * BH * SQ * 4);
+  if (mode == BWA_MODE_ROUNDS_TRANSFER) return XferLayout(BH, SQ, SKV, D, es).total();
   return 0;
 }
 
@@ -144,7 +162,8 @@ bwa_status check_ring(const bwa_tensor* q, const bwa_tensor* k, int n, int mode)
     return fail(BWA_ERR_INVALID_ARG, "n = %d shards must be in [1, S_KV = %lld]", n,
                 (long long)k->S);
   if (n > 4096) return fail(BWA_ERR_UNSUPPORTED, "n = %d above 4096", n);
-  if (mode != BWA_MODE_ROUNDS && mode != BWA_MODE_FUSED && mode != BWA_MODE_SPLIT)
+  if (mode != BWA_MODE_ROUNDS && mode != BWA_MODE_FUSED && mode != BWA_MODE_SPLIT &&
+      mode != BWA_MODE_ROUNDS_TRANSFER)
     return fail(BWA_ERR_INVALID_ARG, "unknown mode %d", mode);
   (void)q;
   return BWA_OK;
@@ -279,7 +298,8 @@ bwa_status bwa_merge_partials(int n, bwa_schedule sched, const float* o_parts,
 size_t bwa_ring_fwd_workspace(const bwa_tensor* q, const bwa_tensor* k, int n, bwa_mode mode) {
   if (!q || !k || q->B <= 0 || q->H <= 0 || q->S < 0 || (q->D != 64 && q->D != 128) || n < 1)
     return 0;
-  return fwd_ws_bytes(q->B * q->H, q->S, (int)q->D, n, mode);
+  if (k->S < 0) return 0;
+  return fwd_ws_bytes(q->B * q->H, q->S, k->S, (int)q->D, elem_size(q->dtype), n, mode);
 }
 
 bwa_status bwa_ring_fwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v, int n,
@@ -295,7 +315,7 @@ bwa_status bwa_ring_fwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tens
   if (q->S == 0) return BWA_OK;
   if (!lse) return fail(BWA_ERR_INVALID_ARG, "lse is NULL");
   const int64_t BH = q->B * q->H;
-  size_t need = fwd_ws_bytes(BH, q->S, (int)q->D, n, mode);
+  size_t need = fwd_ws_bytes(BH, q->S, k->S, (int)q->D, elem_size(q->dtype), n, mode);
   if (need > 0) {
     if (!workspace || ws_bytes < need)
       return fail(BWA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
@@ -305,7 +325,7 @@ bwa_status bwa_ring_fwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tens
   bwa::FwdParams p = base_params(q, k, v, scale, causal);
   p.n = n;
   p.sched = sched;
-  p.mode = mode;
+  p.mode = mode == BWA_MODE_ROUNDS_TRANSFER ? BWA_MODE_ROUNDS : mode;
   p.o = o->ptr;
   p.soB = o->sB; p.soH = o->sH; p.soS = o->sS;
   p.lse = lse;
@@ -322,6 +342,72 @@ bwa_status bwa_ring_fwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tens
       e = bwa::fwd_launch(p, bf, st);
     }
     if (e == hipSuccess) e = bwa::finalize_launch(p, bf, st);
+  } else if (mode == BWA_MODE_ROUNDS_TRANSFER) {
+    // ROUNDS with the exchange made real (device copies into receive slots)
+    const size_t es = elem_size(q->dtype);
+    const XferLayout L(BH, q->S, k->S, (int)q->D, es);
+    char* ws = (char*)workspace;
+    char* slot[2] = {ws + L.o + L.l, ws + L.o + L.l + L.slot};
+    const int64_t row = q->D * (int64_t)es;  // bytes of one Q/K/V row
+    const int64_t qS = q->S, kS = k->S;
+    p.tiles = ceil_div(ceil_div(q->S, n), BM);
+    auto copy = [&](void* dst, const void* src, size_t bytes) {
+      return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st);
+    };
+    if (sched == BWA_SCHED_KV_STATIONARY) {
+      // Q_i, O_i, L_i rotate; slot r % 2 holds every worker's received set
+      for (int r = 0; r < n && e == hipSuccess; ++r) {
+        char* cur = slot[r % 2];
+        float* oc = (float*)(cur + L.q);
+        float* lc = (float*)(cur + L.q + L.o);
+        if (r > 0) {
+          p.q = cur;
+          p.sqS = q->D; p.sqH = qS * q->D; p.sqB = q->H * qS * q->D;
+        }
+        p.o_acc = oc;
+        p.lse = lc;
+        p.round = r;
+        e = bwa::fwd_launch(p, bf, st);
+        if (e != hipSuccess || r + 1 == n) break;
+        char* nx = slot[(r + 1) % 2];
+        if (r == 0)
+          e = bwa::copy_rows_launch(q->ptr, q->sB * es, q->sH * es, q->sS * es, nx, (int)q->B,
+                                    (int)q->H, qS, (int)row, st);
+        else
+          e = copy(nx, cur, (size_t)(BH * qS) * row);
+        if (e == hipSuccess) e = copy(nx + L.q, oc, (size_t)(BH * qS * q->D) * 4);
+        if (e == hipSuccess) e = copy(nx + L.q + L.o, lc, (size_t)(BH * qS) * 4);
+      }
+      if (e == hipSuccess) e = copy(lse, p.lse, (size_t)(BH * qS) * 4);
+      if (e == hipSuccess) e = bwa::finalize_launch(p, bf, st);
+    } else {
+      // K_i, V_i rotate; (O, L) stay with their query block
+      p.o_acc = (float*)ws;
+      for (int r = 0; r < n && e == hipSuccess; ++r) {
+        char* cur = slot[r % 2];
+        if (r > 0) {
+          p.k = cur;
+          p.v = cur + L.kv;
+          p.skS = p.svS = k->D;
+          p.skH = p.svH = kS * k->D;
+          p.skB = p.svB = k->H * kS * k->D;
+        }
+        p.round = r;
+        e = bwa::fwd_launch(p, bf, st);
+        if (e != hipSuccess || r + 1 == n) break;
+        char* nx = slot[(r + 1) % 2];
+        if (r == 0) {
+          e = bwa::copy_rows_launch(k->ptr, k->sB * es, k->sH * es, k->sS * es, nx, (int)k->B,
+                                    (int)k->H, kS, (int)row, st);
+          if (e == hipSuccess)
+            e = bwa::copy_rows_launch(v->ptr, v->sB * es, v->sH * es, v->sS * es, nx + L.kv,
+                                      (int)v->B, (int)v->H, kS, (int)row, st);
+        } else {
+          e = copy(nx, cur, 2 * L.kv);
+        }
+      }
+      if (e == hipSuccess) e = bwa::finalize_launch(p, bf, st);
+    }
   } else if (mode == BWA_MODE_FUSED) {
     p.tiles = ceil_div(ceil_div(q->S, n), BM);
     e = bwa::fwd_launch(p, bf, st);
@@ -356,6 +442,8 @@ bwa_status bwa_ring_bwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tens
   if ((s = check_like(dk, q, k->S, "dk")) != BWA_OK) return s;
   if ((s = check_like(dv, q, k->S, "dv")) != BWA_OK) return s;
   if ((s = check_scale(scale)) != BWA_OK) return s;
+  if (mode == BWA_MODE_ROUNDS_TRANSFER)
+    return fail(BWA_ERR_UNSUPPORTED, "ROUNDS_TRANSFER is a forward mode");
   if ((s = check_ring(q, k, n, mode)) != BWA_OK) return s;
   if ((s = check_sched(sched)) != BWA_OK) return s;
   if (!bwa::bwd_supported(q->dtype, (int)q->D))

@@ -149,4 +149,32 @@ hipError_t finalize_launch(FwdParams p, int dtype_bf16, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Copy a [B, H, S] array of rows (row_bytes each, a multiple of 16) from
+// element-strided storage (strides in bytes) into contiguous storage.
+__global__ __launch_bounds__(256) void copy_rows_kernel(const char* src, int64_t sB, int64_t sH,
+                                                        int64_t sS, char* dst, int B, int H,
+                                                        int64_t S, int row_bytes) {
+  const int per_row = row_bytes / 16;
+  const int64_t total = (int64_t)B * H * S * per_row;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = idx / per_row;
+    const int c = (int)(idx % per_row);
+    const int64_t i = row % S, bh = row / S, b = bh / H, h = bh % H;
+    *(u32x4*)(dst + row * row_bytes + 16 * c) =
+        *(const u32x4*)(src + b * sB + h * sH + i * sS + 16 * c);
+  }
+}
+
+hipError_t copy_rows_launch(const void* src, int64_t sB, int64_t sH, int64_t sS, void* dst, int B,
+                            int H, int64_t S, int row_bytes, hipStream_t st) {
+  const int64_t total = (int64_t)B * H * S * (row_bytes / 16);
+  if (total == 0) return hipSuccess;
+  const int64_t want = (total + 255) / 256;
+  const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(copy_rows_kernel, dim3(blocks), dim3(256), 0, st, (const char*)src, sB, sH,
+                     sS, (char*)dst, B, H, S, row_bytes);
+  return hipGetLastError();
+}
+
 }  // namespace bwa

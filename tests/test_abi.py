@@ -87,6 +87,15 @@ def test_ring_fwd_validation(L):
     expect(L, ring_fwd(L, q, big, k, o), E.BWA_ERR_UNSUPPORTED, "row stride")
 
 
+def test_transfer_workspace_covers_both_schedules(L):
+    q, k = T(S=2048, H=32), T(S=131072, H=32)
+    need = L.bwa_ring_fwd_workspace(ctypes.byref(q), ctypes.byref(k), 8, _bwa.MODE_ROUNDS_TRANSFER)
+    o = 32 * 2048 * 128 * 4
+    kv = 32 * 131072 * 128 * 2
+    assert need >= o + 32 * 2048 * 4 + 2 * (2 * kv)  # stationary (O, L) + two (K, V) slots
+    assert need >= 2 * (32 * 2048 * 128 * 2 + o + 32 * 2048 * 4)  # two (Q, O, L) slots
+
+
 def test_ring_fwd_workspace_checks(L):
     q, k, o = T(S=64), T(S=256), T(S=64)
     need = L.bwa_ring_fwd_workspace(ctypes.byref(q), ctypes.byref(k), 4, _bwa.MODE_ROUNDS)
@@ -147,6 +156,8 @@ def test_ring_bwd_validation(L):
                                                                    kw.get("mode", 1), 0, 0.1] + \
         [ctypes.byref(x) for x in (q, kw.get("dk", k), k)] + [None, 0, None]
     expect(L, L.bwa_ring_bwd(*args(dk=T(S=255))), _bwa.BWA_ERR_INVALID_ARG, "dk")
+    expect(L, L.bwa_ring_bwd(*args(mode=_bwa.MODE_ROUNDS_TRANSFER)), _bwa.BWA_ERR_UNSUPPORTED,
+           "forward mode")
     qf, kf = T(S=64, dtype=0), T(S=256, dtype=0)
     a = [ctypes.byref(x) for x in (qf, kf, kf, qf)] + [FAKE, ctypes.byref(qf), 4, 0, 1, 0, 0.1] + \
         [ctypes.byref(x) for x in (qf, kf, kf)] + [None, 0, None]

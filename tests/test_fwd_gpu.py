@@ -9,7 +9,7 @@ from tests.parity import check_fwd, sample_rows, to64
 
 pytestmark = pytest.mark.gpu
 
-MODES = ["rounds", "fused", "split"]
+MODES = ["rounds", "fused", "split", "rounds_transfer"]
 SCHEDS = ["kv", "q"]
 
 
@@ -269,3 +269,20 @@ def test_split_workspace_merge_matches_ring(bwa):
     o2, lse2 = bwa.bwa_merge_partials(op, lp, 4, "q", dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_transfer_mode_is_bitwise_rounds(bwa, causal):
+    """The emulated exchange moves the rotating blocks through device copies
+    between rounds; the arithmetic is that of ROUNDS, so the results agree bit
+    for bit (also with strided [B, S, H, D] inputs)."""
+    g = torch.Generator().manual_seed(31 + causal)
+    B, H, S, D, n = 1, 3, 700, 128, 5
+    base = [(torch.randn(B, S, H, D, generator=g) * 0.5).bfloat16().cuda() for _ in range(3)]
+    q, k, v = (t.transpose(1, 2) for t in base)  # strided views
+    for sched in SCHEDS:
+        log_case(test="transfer", sched=sched, causal=causal)
+        o1, l1 = bwa.bwa_ring_fwd(q, k, v, n, sched, "rounds", causal=causal)
+        o2, l2 = bwa.bwa_ring_fwd(q, k, v, n, sched, "rounds_transfer", causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), sched
