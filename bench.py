@@ -149,6 +149,26 @@ def summarize_stats(stats_dir: str, workload: str, command: str, top: int = 8) -
     return text
 
 
+def summarize_rounds(trace_dirs, labels, workload: str, n: int, command: str) -> str:
+    """Write profiles/rounds_<workload>.txt: the duration of each of the last n
+    launches of the pair kernel (one per round in ROUNDS mode) from rocprofv3
+    --kernel-trace runs, one per label."""
+    import csv
+    lines = [f"# per-round launches of the pair kernel, workload {workload}, ROUNDS mode, n = {n}",
+             f"# command (from /tmp, per layout): rocprofv3 --kernel-trace --output-format csv "
+             f"-d <dir> -o run -- {command}",
+             "# columns: layout, round 0..n-1 durations in ms, sum"]
+    for d, label in zip(trace_dirs, labels):
+        rows = list(csv.DictReader(open(_find(d, "kernel_trace.csv"))))
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
+                for r in rows if "fwd_bf16_kernel" in r["Kernel_Name"]][-n:]
+        lines.append(f"{label:12s} " + " ".join(f"{x:6.2f}" for x in durs) + f"   sum {sum(durs):.2f}")
+    text = "\n".join(lines) + "\n"
+    with open(os.path.join(ROOT, "profiles", f"rounds_{workload}.txt"), "w") as f:
+        f.write(text)
+    return text
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -159,6 +179,9 @@ def main():
     ap.add_argument("--sched", default="kv", choices=["kv", "q"])
     ap.add_argument("--cpu-rows-per-head", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--striped", action="store_true",
+                    help="causal workloads: rows in the striped order over the n shards "
+                         "(every block pair about half visible)")
     ap.add_argument("--weight-grads", action="store_true",
                     help="recompute workload: also run the gradients through the projection "
                          "(dW_k, dW_v, dy) in every step")
@@ -171,11 +194,19 @@ def main():
     ap.add_argument("--summarize-stats", metavar="STATS_DIR",
                     help="write profiles/kernels_<workload>.txt from a rocprofv3 --stats run "
                          "and exit (no GPU use)")
+    ap.add_argument("--summarize-rounds", nargs=2, metavar=("CONTIGUOUS_DIR", "STRIPED_DIR"),
+                    help="write profiles/rounds_<workload>.txt from two rocprofv3 kernel traces "
+                         "of ROUNDS mode (causal rows in sequence order, then striped) and exit")
     ap.add_argument("--profiled-command", default="python3 bench.py",
                     help="the command line the summarized profiler runs used")
     args = ap.parse_args()
     if args.summarize_traffic:
         print(summarize_traffic(*args.summarize_traffic, args.mode, args.profiled_command))
+        return
+    if args.summarize_rounds:
+        from ring_exact_attention_amd.inputs import WORKLOADS
+        print(summarize_rounds(args.summarize_rounds, ["contiguous", "striped"], args.workload,
+                               WORKLOADS[args.workload].n, args.profiled_command))
         return
     if args.summarize_stats:
         name = args.workload + ("_weight_grads" if args.weight_grads else "")
@@ -226,8 +257,9 @@ def main():
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
 
     def fwd():
-        bwa.bwa_ring_fwd(q, k, v, w.n, args.sched, args.mode, causal=w.causal, scale=w.scale,
-                         o=o, lse=lse, workspace=ws)
+        bwa.bwa_ring_fwd(q, k, v, w.n, args.sched, args.mode,
+                         causal=("striped" if args.striped and w.causal else w.causal),
+                         scale=w.scale, o=o, lse=lse, workspace=ws)
 
     def step():
         if recompute:
@@ -334,7 +366,8 @@ def main():
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "S_Q": w.SQ, "S_KV": w.SKV, "D": w.D,
                    "n_shards": w.n, "schedule": args.sched, "mode": args.mode,
-                   "causal": w.causal, "seed": w.seed},
+                   "causal": ("striped" if args.striped and w.causal else w.causal),
+                   "seed": w.seed},
         "roofline": roofline,
     }
     if not recompute:

@@ -35,8 +35,16 @@
  *   - scale is the softmax scale (callers pass 1/sqrt(D)); it must be finite
  *     and positive.  LSE values are fp32, natural log, scale included.
  *     An empty set of visible keys gives (O = 0, LSE = -inf).
- *   - causal is self-attention masking by position (key j visible to query
- *     i iff j <= i) and requires S_Q == S_KV.
+ *   - causal is self-attention masking by position and requires S_Q == S_KV:
+ *       0: none;
+ *       1: rows are in sequence order, key j visible to query i iff j <= i;
+ *       2: rows are in the striped order over the n shards (bwa_ring_fwd
+ *          only, n must divide S): shard w = rows [w*S/n, (w+1)*S/n) holds
+ *          sequence positions w, w+n, w+2n, ... in order, and key j is
+ *          visible to query i iff its position is not after i's.  Every block
+ *          pair is then about half visible, which balances a causal ring
+ *          (Striped Attention's token assignment, named in the LV-XAttn
+ *          review's references).
  *   - Shards: a length-S sequence split n ways has shard k =
  *     [floor(k*S/n), floor((k+1)*S/n)).  Query blocks and KV shards use the
  *     same split.  Round r pairs for virtual worker w:

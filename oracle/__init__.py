@@ -117,7 +117,18 @@ def _same_dtype(*codes):
     return codes[0]
 
 
-def attn_fwd(q, k, v, scale: float, causal: bool = False, rows=None):
+def _causal_code(causal) -> int:
+    """0: none; 1: positions in row order; ("striped", n): rows in the striped
+    order over n shards (shard w holds positions w, w+n, ...), encoded -n."""
+    if isinstance(causal, tuple):
+        kind, n = causal
+        if kind != "striped" or int(n) < 1:
+            raise ValueError("causal must be a bool or ('striped', n)")
+        return -int(n)
+    return int(bool(causal))
+
+
+def attn_fwd(q, k, v, scale: float, causal=False, rows=None):
     """Unblocked attention.  q [B,H,SQ,D], k/v [B,H,SKV,D].
 
     rows=None returns (O [B,H,SQ,D], LSE [B,H,SQ]) in float64; otherwise rows is
@@ -137,8 +148,8 @@ def attn_fwd(q, k, v, scale: float, causal: bool = False, rows=None):
         nrows, prow = keep.size, keep.ctypes.data
     o = np.zeros((nrows, D), np.float64)
     lse = np.zeros((nrows,), np.float64)
-    _load().orc_attn_fwd_rows(pq, pk, pv, dt, B, H, SQ, SKV, D, float(scale), int(causal),
-                              prow, nrows, o.ctypes.data, lse.ctypes.data)
+    _load().orc_attn_fwd_rows(pq, pk, pv, dt, B, H, SQ, SKV, D, float(scale),
+                              _causal_code(causal), prow, nrows, o.ctypes.data, lse.ctypes.data)
     del kq, kk, kv, keep
     if rows is None:
         return o.reshape(B, H, SQ, D), lse.reshape(B, H, SQ)

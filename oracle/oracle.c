@@ -67,8 +67,24 @@ int orc_num_threads(void) {
 #endif
 }
 
-/* Is key j visible to query i? */
-static int allowed(int causal, int64_t i, int64_t j) { return !causal || j <= i; }
+/* Sequence position held by row i of a striped layout of S rows over n
+ * shards (the token assignment of "Striped attention: Faster ring attention
+ * for causal transformers", named in the LV-XAttn review's references; the
+ * pages give only the title, read as round-robin): shard w = rows
+ * [w*S/n, (w+1)*S/n) holds positions w, w+n, w+2n, ... in order. */
+static int64_t stripe_pos(int64_t i, int64_t S, int64_t n) {
+  int64_t blk = S / n;
+  return (i % blk) * n + i / blk;
+}
+
+/* Is key j visible to query i?  causal: 0 none; 1 key position <= query
+ * position with rows in sequence order; -n the same with rows in the striped
+ * order over n shards (S = sequence length). */
+static int allowed(int causal, int64_t S, int64_t i, int64_t j) {
+  if (causal == 0) return 1;
+  if (causal > 0) return j <= i;
+  return stripe_pos(j, S, -causal) <= stripe_pos(i, S, -causal);
+}
 
 /*
  * Attention of one query row against the keys j in [k0, k1) that it may see:
@@ -79,11 +95,11 @@ static int allowed(int causal, int64_t i, int64_t j) { return !causal || j <= i;
  */
 static double attn_row(const void* q, const void* k, const void* v, int dt,
                        int64_t qrow, int64_t kvbase, int64_t D, int64_t i,
-                       int64_t k0, int64_t k1, double tau, int causal,
+                       int64_t k0, int64_t k1, double tau, int causal, int64_t S,
                        double* s, double* o) {
   double m = -INFINITY;
   for (int64_t j = k0; j < k1; ++j) {
-    if (!allowed(causal, i, j)) { s[j - k0] = -INFINITY; continue; }
+    if (!allowed(causal, S, i, j)) { s[j - k0] = -INFINITY; continue; }
     double dot = 0.0;
     for (int64_t d = 0; d < D; ++d)
       dot += ld(q, dt, qrow * D + d) * ld(k, dt, (kvbase + j) * D + d);
@@ -120,7 +136,7 @@ void orc_attn_fwd_rows(const void* q, const void* k, const void* v, int dt,
     for (int64_t r = 0; r < nrows; ++r) {
       int64_t row = rows ? rows[r] : r;
       int64_t bh = row / SQ, i = row % SQ;
-      lse_out[r] = attn_row(q, k, v, dt, row, bh * SKV, D, i, 0, SKV, tau, causal,
+      lse_out[r] = attn_row(q, k, v, dt, row, bh * SKV, D, i, 0, SKV, tau, causal, SKV,
                             s, o_out + r * D);
     }
     free(s);
@@ -144,7 +160,7 @@ void orc_attn_partial(const void* q, const void* k, const void* v, int dt,
     for (int64_t t = 0; t < B * H * nq; ++t) {
       int64_t bh = t / nq, i = q0 + t % nq;
       int64_t row = bh * SQ + i;
-      lse_out[row] = attn_row(q, k, v, dt, row, bh * SKV, D, i, k0, k1, tau, causal,
+      lse_out[row] = attn_row(q, k, v, dt, row, bh * SKV, D, i, k0, k1, tau, causal, SKV,
                               s, o_out + row * D);
     }
     free(s);
@@ -259,7 +275,7 @@ void orc_attn_bwd_heads(const void* q, const void* k, const void* v, const void*
       for (int64_t i = 0; i < SQ; ++i) {
         double m = -INFINITY;
         for (int64_t j = 0; j < SKV; ++j) {
-          if (!allowed(causal, i, j)) { s[j] = -INFINITY; dp[j] = 0.0; continue; }
+          if (!allowed(causal, SKV, i, j)) { s[j] = -INFINITY; dp[j] = 0.0; continue; }
           double dot = 0.0, dpo = 0.0;
           for (int64_t d = 0; d < D; ++d) {
             dot += ld(q, dt, (qb + i) * D + d) * ld(k, dt, (kb + j) * D + d);
@@ -298,7 +314,7 @@ void orc_attn_bwd_heads(const void* q, const void* k, const void* v, const void*
       double* gv = dv + (t * nk + jj) * D;
       for (int64_t d = 0; d < D; ++d) { gk[d] = 0.0; gv[d] = 0.0; }
       for (int64_t i = 0; i < SQ; ++i) {
-        if (!allowed(causal, i, j) || lse[i] == -INFINITY) continue;
+        if (!allowed(causal, SKV, i, j) || lse[i] == -INFINITY) continue;
         double dot = 0.0, dpo = 0.0;
         for (int64_t d = 0; d < D; ++d) {
           dot += ld(q, dt, (qb + i) * D + d) * ld(k, dt, (kb + j) * D + d);

@@ -142,6 +142,15 @@ def _ptr(t):
     return t.data_ptr()
 
 
+def _causal(c) -> int:
+    """False/True, or "striped" (rows in the striped order over the ring's shards)."""
+    if isinstance(c, str):
+        if c != "striped":
+            raise ValueError(f"unknown causal layout {c!r}")
+        return 2
+    return int(bool(c))
+
+
 def bwa_partial_fwd(q, k, v, q0, nq, k0, nk, scale, causal, o_acc, lse_acc, accumulate):
     """One block pair merged into (o_acc fp32 [B,H,SQ,D], lse_acc fp32 [B,H,SQ])."""
     for name, t in (("o_acc", o_acc), ("lse_acc", lse_acc)):
@@ -149,7 +158,7 @@ def bwa_partial_fwd(q, k, v, q0, nq, k0, nk, scale, causal, o_acc, lse_acc, accu
             raise ValueError(f"{name} must be contiguous float32")
     tq, tk, tv = as_bwa(q), as_bwa(k), as_bwa(v)
     _check(lib().bwa_partial_fwd(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), q0, nq, k0,
-                                 nk, float(scale), int(bool(causal)), _ptr(o_acc), _ptr(lse_acc),
+                                 nk, float(scale), _causal(causal), _ptr(o_acc), _ptr(lse_acc),
                                  int(bool(accumulate)), _stream(q.device)))
 
 
@@ -231,7 +240,7 @@ def bwa_ring_fwd(q, k, v, n, sched="kv", mode="fused", causal=False, scale=None,
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     tq, tk, tv, to = as_bwa(q), as_bwa(k), as_bwa(v), as_bwa(o)
     _check(lib().bwa_ring_fwd(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), int(n),
-                              _sched(sched), m, int(bool(causal)), float(scale), ctypes.byref(to),
+                              _sched(sched), m, _causal(causal), float(scale), ctypes.byref(to),
                               _ptr(lse), _ptr(ws), nbytes, _stream(q.device)))
     return o, lse
 
@@ -257,7 +266,7 @@ def bwa_ring_bwd(q, k, v, o, lse, dout, n, sched="kv", mode="fused", causal=Fals
     t = [as_bwa(x) for x in (q, k, v, o, dout, dq, dk, dv)]
     _check(lib().bwa_ring_bwd(ctypes.byref(t[0]), ctypes.byref(t[1]), ctypes.byref(t[2]),
                               ctypes.byref(t[3]), _ptr(lse), ctypes.byref(t[4]), int(n),
-                              _sched(sched), m, int(bool(causal)), float(scale),
+                              _sched(sched), m, _causal(causal), float(scale),
                               ctypes.byref(t[5]), ctypes.byref(t[6]), ctypes.byref(t[7]),
                               _ptr(ws), nbytes, _stream(q.device)))
     return dq, dk, dv

@@ -91,6 +91,8 @@ bwa_status check_qkv(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor*
     return fail(BWA_ERR_INVALID_ARG, "q, k, v batch/head counts differ");
   if (q->D != k->D || q->D != v->D) return fail(BWA_ERR_INVALID_ARG, "q, k, v head dims differ");
   if (k->S != v->S) return fail(BWA_ERR_INVALID_ARG, "k and v lengths differ");
+  if (causal < 0 || causal > 2)
+    return fail(BWA_ERR_INVALID_ARG, "causal must be 0, 1 (sequence order) or 2 (striped)");
   if (causal && q->S != k->S)
     return fail(BWA_ERR_UNSUPPORTED, "causal masking needs S_Q == S_KV (self-attention)");
   return BWA_OK;
@@ -149,7 +151,7 @@ bwa::FwdParams base_params(const bwa_tensor* q, const bwa_tensor* k, const bwa_t
   p.SQ = (int)q->S;
   p.SKV = (int)k->S;
   p.D = (int)q->D;
-  p.causal = causal ? 1 : 0;
+  p.causal = causal;
   p.scale = scale;
   p.scale_log2 = scale * bwa::kLog2e;
   return p;
@@ -225,6 +227,8 @@ bwa_status bwa_partial_fwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_t
                            void* stream) {
   bwa_status s;
   if ((s = check_qkv(q, k, v, causal)) != BWA_OK) return s;
+  if (causal == 2)
+    return fail(BWA_ERR_UNSUPPORTED, "the striped order is defined by a ring's shards (ring_fwd)");
   if ((s = check_scale(scale)) != BWA_OK) return s;
   if (q0 < 0 || nq < 0 || q0 + nq > q->S)
     return fail(BWA_ERR_INVALID_ARG, "query range [%lld, %lld) outside [0, %lld)",
@@ -322,8 +326,11 @@ bwa_status bwa_ring_fwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tens
     if ((uintptr_t)workspace % 256 != 0)
       return fail(BWA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   }
+  if (causal == 2 && q->S % n != 0)
+    return fail(BWA_ERR_UNSUPPORTED, "striped causal order needs n to divide S");
   bwa::FwdParams p = base_params(q, k, v, scale, causal);
   p.n = n;
+  p.blk = causal == 2 ? q->S / n : 0;
   p.sched = sched;
   p.mode = mode == BWA_MODE_ROUNDS_TRANSFER ? BWA_MODE_ROUNDS : mode;
   p.o = o->ptr;
@@ -444,6 +451,7 @@ bwa_status bwa_ring_bwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tens
   if ((s = check_scale(scale)) != BWA_OK) return s;
   if (mode == BWA_MODE_ROUNDS_TRANSFER)
     return fail(BWA_ERR_UNSUPPORTED, "ROUNDS_TRANSFER is a forward mode");
+  if (causal == 2) return fail(BWA_ERR_UNSUPPORTED, "striped causal order is forward only");
   if ((s = check_ring(q, k, n, mode)) != BWA_OK) return s;
   if ((s = check_sched(sched)) != BWA_OK) return s;
   if (!bwa::bwd_supported(q->dtype, (int)q->D))

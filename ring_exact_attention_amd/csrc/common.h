@@ -57,7 +57,9 @@ struct FwdParams {
   float* o_acc;     // EPI_ACC running O fp32 [B,H,SQ,D]; EPI_PART partial O [n][B,H,SQ,D]
   float* lse_part;  // EPI_PART partial LSE [n][B,H,SQ]
   int B, H, SQ, SKV, D, n;
-  int sched, mode, causal, round;
+  int sched, mode, round;
+  int causal;   // 0 none, 1 rows in sequence order, 2 rows in the striped order
+  int64_t blk;  // causal == 2: rows per shard (S / n)
   int tiles;   // query tiles per group
   int groups;  // groups of tiles (each group shares one KV range at a time)
   int accumulate;
@@ -146,6 +148,10 @@ __device__ inline bool make_job(const FwdParams& p, int BM, Job* jb) {
 
 // KV segment [*k0, *k1) of step r of a job (empty when nothing is visible).
 // Under causal masking no key at or beyond the job's last row + 1 is visible.
+// In the striped order (shard w holds positions w, w+n, ...; a row's shard w
+// and index c give position c*n + w) a row at (w, c) sees the first c + 1
+// keys of shards up to w and the first c keys of later shards, so a shard is
+// cut after the job's largest such count.
 __device__ inline void job_segment(const FwdParams& p, const Job& jb, int r, int64_t* k0,
                                    int64_t* k1) {
   if (p.single_pair) {
@@ -156,7 +162,12 @@ __device__ inline void job_segment(const FwdParams& p, const Job& jb, int r, int
     *k0 = shard_start(p.SKV, p.n, kb);
     *k1 = shard_start(p.SKV, p.n, kb + 1);
   }
-  if (p.causal && *k1 > jb.r1) *k1 = jb.r1;
+  if (p.causal == 1 && *k1 > jb.r1) *k1 = jb.r1;
+  if (p.causal == 2) {
+    const int64_t w0 = jb.r0 / p.blk, w1 = (jb.r1 - 1) / p.blk, ks = *k0 / p.blk;
+    const int64_t cnt = w0 == w1 ? (jb.r1 - 1) % p.blk + (ks <= w1 ? 1 : 0) : p.blk;
+    if (*k1 > *k0 + cnt) *k1 = *k0 + cnt;
+  }
   if (*k1 < *k0) *k1 = *k0;
 }
 

@@ -52,10 +52,22 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // Number of leading keys of a tile starting at key kt that a query row may see:
 // keys kt .. kt+lim-1 are visible (segment end ke; under causal masking only
-// keys <= row).  Clamped to [0, bn].
-__device__ inline int visible_prefix(int64_t kt, int64_t ke, int causal, int64_t row, int bn) {
+// keys at or before the row's position).  Clamped to [0, bn].
+//   causal == 1: rows and keys in sequence order, key j visible iff j <= row.
+//   causal == 2: striped order over shards of blk rows (shard w holds
+//     positions w, w+n, ...): the row at (shard w, index c) sees the first
+//     c + 1 keys of shards <= w and the first c keys of later shards; a tile
+//     lies inside one shard (ks, starting at index c0).  (row_w, row_c) is the
+//     row's (shard, index).
+__device__ inline int visible_prefix(int64_t kt, int64_t ke, int causal, int64_t row, int bn,
+                                     int64_t blk, int64_t row_w, int64_t row_c) {
   int64_t lim = ke - kt;
-  if (causal && row + 1 - kt < lim) lim = row + 1 - kt;
+  if (causal == 1 && row + 1 - kt < lim) lim = row + 1 - kt;
+  if (causal == 2) {
+    const int64_t ks = kt / blk, c0 = kt - ks * blk;
+    const int64_t see = row_c + (ks <= row_w ? 1 : 0) - c0;
+    if (see < lim) lim = see;
+  }
   return (int)(lim < 0 ? 0 : (lim > bn ? bn : lim));
 }
 
@@ -141,6 +153,8 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
   const int64_t wrow0 = jb.r0 + wave * 32;
   const int64_t myrow = wrow0 + lr;
   const bool row_ok = myrow < jb.r1;
+  const int64_t row_w = p.causal == 2 ? myrow / p.blk : 0;  // striped: shard, index
+  const int64_t row_c = p.causal == 2 ? myrow - row_w * p.blk : 0;
   bf16x8 qreg[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s)
@@ -238,9 +252,12 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
   };
   const float c2 = p.scale_log2;
   auto phase_softmax = [&](const TileIter& t) {
-    const bool need_mask = (t.kt + BN > t.ke) || (p.causal && t.kt + BN - 1 > wrow0);
+    bool need_mask = (t.kt + BN > t.ke) || (p.causal == 1 && t.kt + BN - 1 > wrow0);
+    if (p.causal == 2)
+      need_mask = __builtin_amdgcn_ballot_w64(
+                      visible_prefix(t.kt, t.ke, 2, myrow, BN, p.blk, row_w, row_c) < BN) != 0;
     if (need_mask) {
-      const int lim = visible_prefix(t.kt, t.ke, p.causal, myrow, BN);
+      const int lim = visible_prefix(t.kt, t.ke, p.causal, myrow, BN, p.blk, row_w, row_c);
 #pragma unroll
       for (int u = 0; u < BN / 32; ++u)
 #pragma unroll
@@ -391,6 +408,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
   const int sub = tid & 3;  // which quarter of D this lane owns
   const int64_t myrow = jb.r0 + (tid >> 2);
   const bool row_ok = myrow < jb.r1;
+  const int64_t row_w = p.causal == 2 ? myrow / p.blk : 0;  // striped: shard, index
+  const int64_t row_c = p.causal == 2 ? myrow - row_w * p.blk : 0;
   const int b = jb.bh / p.H, h = jb.bh % p.H;
   const float* qg = (const float*)p.q + b * p.sqB + h * p.sqH;
   const float* kg = (const float*)p.k + b * p.skB + h * p.skH;
@@ -420,6 +439,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
   if (!it.valid(jb) && jb.epi == EPI_ACC && jb.acc_in) return;
   const float c2 = p.scale_log2;
   for (; it.valid(jb); it.advance(p, jb, BN)) {
+    // keys it.kt + j, j < lim, are visible to this row
+    const int lim = visible_prefix(it.kt, it.ke, p.causal, myrow, BN, p.blk, row_w, row_c);
     __syncthreads();
     for (int c = tid; c < BN * D / 4; c += C::NT) {
       int row = c / (D / 4), col4 = c % (D / 4);
@@ -441,9 +462,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
       for (int e = 0; e < DL; ++e) dot = __builtin_fmaf(qv[e], Ks[j * KS + sub * DL + e], dot);
       dot += __shfl_xor(dot, 1);
       dot += __shfl_xor(dot, 2);
-      int64_t key = it.kt + j;
-      bool vis = key < it.ke && (!p.causal || key <= myrow);
-      if (!vis) continue;  // uniform across the four lanes of a row
+      if (j >= lim) continue;  // uniform across the four lanes of a row
       const float t = dot * c2;
       const float m_new = fmaxf(m2, t);
       const float alpha = fast_exp2(m2 - m_new);

@@ -71,6 +71,9 @@ def test_ring_fwd_validation(L):
     expect(L, ring_fwd(L, q, k, k, o, n=0), E.BWA_ERR_INVALID_ARG, "shards")
     expect(L, ring_fwd(L, q, k, k, o, n=257), E.BWA_ERR_INVALID_ARG, "shards")
     expect(L, ring_fwd(L, q, k, k, o, causal=1), E.BWA_ERR_UNSUPPORTED, "causal")
+    expect(L, ring_fwd(L, q, k, k, o, causal=3), E.BWA_ERR_INVALID_ARG, "causal must be")
+    sq = T(S=300)
+    expect(L, ring_fwd(L, sq, sq, sq, sq, n=7, causal=2), E.BWA_ERR_UNSUPPORTED, "divide")
     expect(L, ring_fwd(L, q, k, T(S=256, dtype=0), o), E.BWA_ERR_INVALID_ARG, "dtype")
     expect(L, ring_fwd(L, q, k, T(S=255), o), E.BWA_ERR_INVALID_ARG, "lengths differ")
     expect(L, ring_fwd(L, q, k, k, T(S=63)), E.BWA_ERR_INVALID_ARG, "o:")

@@ -286,3 +286,48 @@ def test_transfer_mode_is_bitwise_rounds(bwa, causal):
         o2, l2 = bwa.bwa_ring_fwd(q, k, v, n, sched, "rounds_transfer", causal=causal)
         torch.cuda.synchronize()
         assert torch.equal(o1, o2) and torch.equal(l1, l2), sched
+
+
+def _stripe_inverse(S, n):
+    """Row of the striped layout holding each sequence position (shard w holds
+    positions w, w+n, ...), from dealing positions round-robin to shards."""
+    shards = [[] for _ in range(n)]
+    for t in range(S):
+        shards[t % n].append(t)
+    pos = np.array([t for sh in shards for t in sh])
+    return np.argsort(pos)
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 512, 128, 4), (1, 1, 384, 64, 3), (2, 2, 1024, 128, 8)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_striped_causal_all_modes(bwa, orc, shape):
+    """Rows in the striped order (shard w holds positions w, w+n, ...): every
+    mode and schedule against the oracle's causal attention on the sequence."""
+    B, H, S, D, n = shape
+    g = torch.Generator().manual_seed(S + n)
+    q, k, v = [(torch.randn(B, H, S, D, generator=g) * 0.5).bfloat16() for _ in range(3)]
+    scale = 1.0 / math.sqrt(D)
+    O, L = orc.attn_fwd(q, k, v, scale, causal=("striped", n))
+    inv = _stripe_inverse(S, n)
+    On, Ln = orc.attn_fwd(q[:, :, inv], k[:, :, inv], v[:, :, inv], scale, causal=True)
+    np.testing.assert_allclose(O[:, :, inv], On, rtol=1e-12, atol=1e-13)  # oracle self-check
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    for mode in MODES:
+        for sched in SCHEDS:
+            log_case(test="striped", shape=shape, mode=mode, sched=sched)
+            o, lse = bwa.bwa_ring_fwd(qd, kd, vd, n, sched, mode, causal="striped", scale=scale)
+            torch.cuda.synchronize()
+            check_fwd(o, lse, O, L, "bf16", f"striped {shape} {mode} {sched}")
+
+
+def test_striped_causal_f32(bwa, orc):
+    B, H, S, D, n = 1, 1, 96, 64, 4
+    g = torch.Generator().manual_seed(5)
+    q, k, v = [torch.randn(B, H, S, D, generator=g) for _ in range(3)]
+    O, L = orc.attn_fwd(q, k, v, 0.125, causal=("striped", n))
+    for mode in MODES:
+        log_case(test="striped f32", mode=mode)
+        o, lse = bwa.bwa_ring_fwd(q.cuda(), k.cuda(), v.cuda(), n, "kv", mode, causal="striped",
+                                  scale=0.125)
+        torch.cuda.synchronize()
+        check_fwd(o, lse, O, L, "f32", f"striped f32 {mode}")

@@ -525,3 +525,35 @@ def test_recompute_grads_are_adjoints(orc):
     dy_v = orc.kv_grad_y(zero_g, g, w, W)
     np.testing.assert_allclose(orc.kv_grad_y(g, g, w, W), dy_k + dy_v, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(dy_v, orc.kv_grad_y(g, zero_g, W, w), rtol=0, atol=0)
+
+
+# ---------------------------------------------------------------- striped causal layout
+
+def stripe_positions(S, n):
+    """Sequence position of each row of the striped layout: shard w (rows
+    [w*S/n, (w+1)*S/n)) holds positions w, w+n, w+2n, ...  Built by dealing
+    the positions 0..S-1 round-robin to the n shards."""
+    shards = [[] for _ in range(n)]
+    for t in range(S):
+        shards[t % n].append(t)
+    return np.array([t for sh in shards for t in sh])
+
+
+def test_striped_causal_is_causal_on_positions(orc):
+    """Causal attention over rows in the striped order is ordinary causal
+    attention on the sequence, with rows reordered by their positions."""
+    for (S, n) in [(12, 3), (16, 4), (10, 1)]:
+        B, H, D = 1, 2, 4
+        q, k, v = rnd((B, H, S, D), 180), rnd((B, H, S, D), 181), rnd((B, H, S, D), 182)
+        pos = stripe_positions(S, n)
+        assert sorted(pos.tolist()) == list(range(S))
+        inv = np.argsort(pos)  # row of the striped layout holding each position
+        O, L = orc.attn_fwd(q, k, v, 0.4, causal=("striped", n))
+        # natural order: position t is row inv[t] of the striped tensors
+        On, Ln = orc.attn_fwd(q[:, :, inv], k[:, :, inv], v[:, :, inv], 0.4, causal=True)
+        np.testing.assert_allclose(O[:, :, inv], On, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(L[:, :, inv], Ln, rtol=1e-13, atol=1e-14)
+    # row 0 of the striped layout holds position 0: it sees only itself
+    q, k, v = rnd((1, 1, 16, 4), 183), rnd((1, 1, 16, 4), 184), rnd((1, 1, 16, 4), 185)
+    O, L = orc.attn_fwd(q, k, v, 0.4, causal=("striped", 4))
+    np.testing.assert_allclose(O[:, :, 0], v[:, :, 0], rtol=1e-13)

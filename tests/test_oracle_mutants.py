@@ -25,7 +25,8 @@ MUTANTS = {
                               "double wb = exp(la[r] - L), wa = exp(lb[r] - L);"),
     "merge_plain_sum": ("double L = M + log(exp(la[r] - M) + exp(lb[r] - M));",
                         "double L = M;"),
-    "causal_strict": ("return !causal || j <= i;", "return !causal || j < i;"),
+    "causal_strict": ("if (causal > 0) return j <= i;", "if (causal > 0) return j < i;"),
+    "stripe_transposed": ("return (i % blk) * n + i / blk;", "return (i / blk) * n + i % blk;"),
     "ring_wrong_direction": ("int64_t moved = ((w - r) % n + n) % n;",
                              "int64_t moved = ((w + r) % n + n) % n;"),
     "ring_stationary_swapped": ("if (sched == 0) { *qblk = moved; *kblk = w; }",
@@ -80,6 +81,7 @@ def all_pins(orc):
         lambda: pins.test_schedule_model_speedup_closed_form(orc),
         lambda: pins.test_schedule_model_choices(orc),
         lambda: pins.test_recompute_grads_vs_numpy(orc),
+        lambda: pins.test_striped_causal_is_causal_on_positions(orc),
         lambda: pins.test_recompute_grads_are_adjoints(orc),
     ]
     return calls
