@@ -120,7 +120,13 @@ __device__ inline void store4<bf16>(bf16* dst, float a, float b, float c, float 
 template <int D_>
 struct Bf16Fwd {
   static constexpr int D = D_, NW = 8, NT = 512, BM = 256, BN = 64;
-  static constexpr int KS = D + 8, VS = D + 16;  // padded LDS row strides (elements)
+  // Padded LDS row strides (elements).  K rows are read 16 bytes per lane by
+  // ds_read_b128.  A transposing V read covers 8 rows x 64 bytes and is served
+  // 32 lanes (4 rows) at a time from 64 banks of 4 bytes: rows 2*(D+32) bytes
+  // apart land in distinct 64-byte quarters of the bank space (the stride is
+  // 64 or 192 mod 256), so the read is conflict-free; D+16 would pair rows
+  // on the same banks and halve the read rate.
+  static constexpr int KS = D + 8, VS = D + 32;
   static constexpr int K_TILE = BN * KS, V_TILE = BN * VS;
   static constexpr int STAGE = K_TILE + V_TILE;
   static constexpr int NBUF = 3;
@@ -139,7 +145,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
   if (!make_job(p, C::BM, &jb)) return;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   const int lr = lane & 31;
   const int g = lane >> 5;
@@ -207,7 +213,8 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < C::KC; ++i) {
       const int r = min(srow0 + i * srstep, lim - 1);
-      stg[i] = *(const u32x4*)(base + __umul24((uint32_t)r, sstr2) + scol8 * 16);
+      const uint32_t off = __umul24((uint32_t)r, sstr2) + (uint32_t)(scol8 * 16);
+      stg[i] = *(const u32x4*)(base + off);  // uniform base + 32-bit lane offset
     }
   };
   auto load_tile = [&](const TileIter& t) {
