@@ -489,6 +489,8 @@ bwa_status bwa_kv_recompute(const void* y, const void* wk_t, const void* wv_t, i
   if (E % 64 != 0) return fail(BWA_ERR_UNSUPPORTED, "E must be a multiple of 64");
   if ((H * D) % 128 != 0) return fail(BWA_ERR_UNSUPPORTED, "H*D must be a multiple of 128");
   if (B * S_KV >= kMaxDim || E >= kMaxDim) return fail(BWA_ERR_UNSUPPORTED, "sizes too large");
+  if ((B * S_KV) * E * 2 >= ((int64_t)1 << 32) || (H * D) * E * 2 >= ((int64_t)1 << 32))
+    return fail(BWA_ERR_UNSUPPORTED, "y and each W must be smaller than 4 GiB");
   bwa_status s;
   if ((s = check_tensor(k, "k", true)) != BWA_OK) return s;
   if ((s = check_tensor(v, "v", true)) != BWA_OK) return s;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace bwa {
 
 typedef __bf16 bf16;
@@ -22,6 +24,16 @@ constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 enum Mode { MODE_ROUNDS = 0, MODE_FUSED = 1, MODE_SPLIT = 2 };
 enum Sched { SCHED_KV_STATIONARY = 0, SCHED_Q_STATIONARY = 1 };
 enum Epilogue { EPI_FINAL = 0, EPI_ACC = 1, EPI_PART = 2 };
+
+// Calls f(integral_constant<int, i>) for i = B .. E-1: compile-time indices for
+// scheduling builtins and register arrays in hand-ordered instruction streams.
+template <int B, int E, typename F>
+__device__ inline __attribute__((always_inline)) void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // Start of shard k of a length-S sequence split n ways: floor(k*S/n).
 __host__ __device__ inline int64_t shard_start(int64_t S, int n, int k) {

@@ -16,6 +16,13 @@
 // 128 x 64 per wave (4 x 2 MFMA blocks, fp32 accumulators), 64 e per LDS
 // stage (128 contiguous bytes per row and load), double buffered in 144 KB of
 // LDS with rows padded by 16 bytes (conflict-free 16-byte operand reads).
+// Within a stage the 32 MFMAs of a wave are issued in a fixed order, the
+// operands of each 16-element k-step read during the previous one; the
+// chunks staged for the next stage go to the other buffer one per MFMA at
+// the head of the stage, and the global loads of the stage after that are
+// issued one per MFMA at its tail (so their data has a whole stage to land).
+// Bursts of wide LDS writes fill the LDS data FIFO and stall every wave's
+// LDS reads; spreading them and the reads over the MFMAs is worth 14% here.
 // Workgroups that share a y tile are placed consecutively on one XCD so the
 // tile is read from HBM once and served from that XCD's L2; W (both
 // projections, 64 MB) stays in the MALL.
@@ -74,37 +81,36 @@ __global__ __launch_bounds__(T::NT) void gemm_kv_kernel(GemmParams p) {
   const bf16* wsrc = p.w[proj];
 
   // thread's chunks: passes i < KA are W rows, the rest y rows; 8-lane groups
-  // cover one row's GK elements (128 contiguous bytes for GK = 64)
+  // cover one row's GK elements (128 contiguous bytes for GK = 64).  Rows past
+  // the end repeat the last row.  Byte offsets from the operand's base fit in
+  // 32 bits (rows x E x 2 < 2^31, checked on the host).
+  uint32_t goff[KC];
+  bf16* sdst[KC];
+  const bf16* ysrc = p.y;
+#pragma unroll
+  for (int i = 0; i < KC; ++i) {
+    const int c = tid + T::NT * i;
+    bf16* As0 = smem;
+    if (i < KA) {
+      const int row = c / CPR, col8 = c % CPR;
+      const int n = min(n0 + row, p.HD - 1);
+      goff[i] = ((uint32_t)n * (uint32_t)p.E + (uint32_t)(col8 * 8)) * 2u;
+      sdst[i] = As0 + row * GS + col8 * 8;
+    } else {
+      const int cb = c - GM * CPR;
+      const int row = cb / CPR, col8 = cb % CPR;
+      const int sr = min(s0 + row, p.BS - 1);
+      goff[i] = ((uint32_t)sr * (uint32_t)p.E + (uint32_t)(col8 * 8)) * 2u;
+      sdst[i] = As0 + T::A_EL + row * GS + col8 * 8;
+    }
+  }
   u32x4 stg[KC];
-  auto load = [&](int e0) {
-#pragma unroll
-    for (int i = 0; i < KC; ++i) {
-      const int c = tid + T::NT * i;
-      if (i < KA) {
-        const int row = c / CPR, col8 = c % CPR;
-        const int n = min(n0 + row, p.HD - 1);
-        stg[i] = *(const u32x4*)(wsrc + (int64_t)n * p.E + e0 + col8 * 8);
-      } else {
-        const int cb = c - GM * CPR;
-        const int row = cb / CPR, col8 = cb % CPR;
-        const int sr = min(s0 + row, p.BS - 1);
-        stg[i] = *(const u32x4*)(p.y + (int64_t)sr * p.E + e0 + col8 * 8);
-      }
-    }
+  auto load1 = [&](int i, int e0) __attribute__((always_inline)) {
+    const char* base = (const char*)((i < KA ? wsrc : ysrc) + e0);
+    stg[i] = *(const u32x4*)(base + goff[i]);
   };
-  auto store = [&](int buf) {
-    bf16* As = smem + buf * (T::A_EL + T::B_EL);
-    bf16* Bs = As + T::A_EL;
-#pragma unroll
-    for (int i = 0; i < KC; ++i) {
-      const int c = tid + T::NT * i;
-      if (i < KA) {
-        *(u32x4*)(As + (c / CPR) * GS + (c % CPR) * 8) = stg[i];
-      } else {
-        const int cb = c - GM * CPR;
-        *(u32x4*)(Bs + (cb / CPR) * GS + (cb % CPR) * 8) = stg[i];
-      }
-    }
+  auto store1 = [&](int i, int buf) __attribute__((always_inline)) {
+    *(u32x4*)(sdst[i] + buf * (T::A_EL + T::B_EL)) = stg[i];
   };
 
   f32x16 acc[T::FA][T::FB];
@@ -113,36 +119,65 @@ __global__ __launch_bounds__(T::NT) void gemm_kv_kernel(GemmParams p) {
 #pragma unroll
     for (int b = 0; b < T::FB; ++b) acc[a][b] = f32x16{};
 
+  // operand reads: A rows (n) of this wave's block a, B rows (s) of block b,
+  // 16 contraction elements at step ks
+  const bf16* aread = smem + (wm * T::WTM + lr) * GS + 8 * g;
+  const bf16* bread = smem + T::A_EL + (wn * T::WTN + lr) * GS + 8 * g;
+  constexpr int NOP = T::FA + T::FB, KSN = GK / 16, NM = KSN * T::FA * T::FB;
+  auto rd = [&](int buf, int ks, int o) __attribute__((always_inline)) {
+    const int bo = buf * (T::A_EL + T::B_EL) + 16 * ks;
+    return o < T::FA ? *(const bf16x8*)(aread + bo + 32 * o * GS)
+                     : *(const bf16x8*)(bread + bo + 32 * (o - T::FA) * GS);
+  };
+
+  // One stage: the MFMAs of buffer buf in a fixed issue order, each k-step's
+  // operands read during the previous k-step, and (WR) the staged chunks of
+  // the next stage written into buf^1 one per MFMA, then (LD) the loads of
+  // the stage after it issued one per MFMA, so neither the LDS writes nor
+  // the global loads arrive in bursts.
+  auto stage = [&](auto wr_, auto ld_, int buf, int e_next) __attribute__((always_inline)) {
+    constexpr bool WR = decltype(wr_)::value, LD = decltype(ld_)::value;
+    bf16x8 op[2][NOP];
+#pragma unroll
+    for (int o = 0; o < NOP; ++o) op[0][o] = rd(buf, 0, o);
+    static_for<0, NM>([&](auto mi) __attribute__((always_inline)) {
+      constexpr int m = decltype(mi)::value;
+      constexpr int ks = m / (T::FA * T::FB), idx = m % (T::FA * T::FB);
+      constexpr int a = idx / T::FB, b = idx % T::FB;
+      __builtin_amdgcn_sched_barrier(0);
+      acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[ks & 1][a], op[ks & 1][T::FA + b],
+                                                          acc[a][b], 0, 0, 0);
+      if constexpr (ks + 1 < KSN && idx < NOP) op[(ks + 1) & 1][idx] = rd(buf, ks + 1, idx);
+      if constexpr (WR && m < KC) store1(m, buf ^ 1);
+      if constexpr (LD && m >= NM - KC) load1(m - (NM - KC), e_next);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
   const int nk = p.E / GK;
-  load(0);
-  store(0);
-  __syncthreads();
-  int buf = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) load((kt + 1) * GK);
-    const bf16* As = smem + buf * (T::A_EL + T::B_EL);
-    const bf16* Bs = As + T::A_EL;
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  // prologue: stage 0 in buffer 0, stage 1 in flight
 #pragma unroll
-    for (int ks = 0; ks < GK / 16; ++ks) {
-      bf16x8 av[T::FA], bv[T::FB];
+  for (int i = 0; i < KC; ++i) load1(i, 0);
 #pragma unroll
-      for (int a = 0; a < T::FA; ++a)
-        av[a] = *(const bf16x8*)(As + (wm * T::WTM + 32 * a + lr) * GS + 16 * ks + 8 * g);
+  for (int i = 0; i < KC; ++i) store1(i, 0);
+  if (nk > 1) {
 #pragma unroll
-      for (int b = 0; b < T::FB; ++b)
-        bv[b] = *(const bf16x8*)(Bs + (wn * T::WTN + 32 * b + lr) * GS + 16 * ks + 8 * g);
-#pragma unroll
-      for (int a = 0; a < T::FA; ++a)
-#pragma unroll
-        for (int b = 0; b < T::FB; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
-    }
-    if (!more) break;
-    store(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
+    for (int i = 0; i < KC; ++i) load1(i, GK);
   }
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 2 < nk; ++kt) {
+    stage(T_{}, T_{}, kt & 1, (kt + 2) * GK);
+    __syncthreads();
+  }
+  if (kt + 1 < nk) {
+    stage(T_{}, F_{}, kt & 1, 0);
+    __syncthreads();
+    ++kt;
+  }
+  stage(F_{}, F_{}, kt & 1, 0);
 
   bf16* out = p.out[proj];
 #pragma unroll

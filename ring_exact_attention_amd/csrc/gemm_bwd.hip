@@ -6,7 +6,9 @@
 // with W_k^T the [H*D, E] weight layout of bwa_kv_recompute.
 //
 // Both are 256 x 256-tiled MFMA GEMMs on 8 waves (2 x 4, 128 x 64 per wave),
-// 64 contraction rows per LDS stage, double buffered.  An operand whose
+// 64 contraction rows per LDS stage, double buffered, with the MFMAs of a
+// stage in a fixed order beside the operand reads of the next k-step, the
+// LDS writes of the next stage and the global loads of the one after.  An operand whose
 // contraction index is its storage row (dK and y in the weight gradient, W^T
 // in dy) is staged row-major as [k][m] and read with ds_read_b64_tr_b16: each
 // lane takes rows k0..k0+3 and k0+4..k0+7 of its column, the same k order as
@@ -22,7 +24,10 @@ constexpr int TM = 256, TN = 256, TK = 64;  // workgroup tile
 constexpr int NT = 512;                     // 8 waves: 2 (m) x 4 (n)
 constexpr int WTM = 128, WTN = 64;          // per wave
 constexpr int FA = WTM / 32, FB = WTN / 32; // 32x32 blocks per wave
-constexpr int TSK = TM + 16;                // row stride of a [k][m] tile (elements)
+// Row stride of a [k][m] tile (elements): a transposing read serves 32 lanes
+// as 4 rows x 64 bytes from 64 banks of 4 bytes; rows 2*(TM+32) bytes apart
+// (64 mod 256) fall in distinct quarters of the bank space, conflict-free.
+constexpr int TSK = TM + 32;
 constexpr int NSK = TK + 8;                 // row stride of a [m][k] tile (elements)
 constexpr int T_EL = TK * TSK;              // [k][m] tile elements (TM == TN)
 constexpr int N_EL = TM * NSK;              // [m][k] tile elements
@@ -51,24 +56,45 @@ __device__ inline bf16x8 read_t(const bf16* t, int k0, int m0, int lane) {
   return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
 }
 
-__device__ inline void mma_stage(const bf16* As, bool a_t, const bf16* Bs, int wm, int wn, int lane,
-                                 f32x16 (&acc)[FA][FB]) {
+// Operand o of k-step ks: o < FA is A block o (rows m of this wave), the
+// rest B block o - FA (columns n).  A is [k][m] (AT) or [m][k]; B is [k][n].
+template <bool AT>
+__device__ inline bf16x8 read_op(const bf16* As, const bf16* Bs, int ks, int o, int wm, int wn,
+                                 int lane) {
   const int lr = lane & 31, g = lane >> 5;
+  if (o < FA)
+    return AT ? read_t(As, 16 * ks + 8 * g, wm * WTM + 32 * o, lane)
+              : *(const bf16x8*)(As + (wm * WTM + 32 * o + lr) * NSK + 16 * ks + 8 * g);
+  return read_t(Bs, 16 * ks + 8 * g, wn * WTN + 32 * (o - FA), lane);
+}
+
+// One stage of MFMAs from (As, Bs) in a fixed issue order, each k-step's
+// operands read during the previous one.  Chunk hooks run beside the MFMAs:
+// write(i) for i < NCH at the head (the next stage's staged chunks into the
+// other buffer) and load(i) at the tail (the loads of the stage after it),
+// so neither LDS writes nor global loads come in bursts.
+constexpr int NCH = 8;  // 16-byte staging chunks per thread and stage
+template <bool AT, bool WR, bool LD, typename W, typename L>
+__device__ inline __attribute__((always_inline)) void mma_stage(
+    const bf16* As, const bf16* Bs, int wm, int wn, int lane, f32x16 (&acc)[FA][FB], W&& write,
+    L&& load) {
+  constexpr int NOP = FA + FB, KSN = TK / 16, NM = KSN * FA * FB;
+  bf16x8 op[2][NOP];
 #pragma unroll
-  for (int ks = 0; ks < TK / 16; ++ks) {
-    bf16x8 av[FA], bv[FB];
-#pragma unroll
-    for (int a = 0; a < FA; ++a)
-      av[a] = a_t ? read_t(As, 16 * ks + 8 * g, wm * WTM + 32 * a, lane)
-                  : *(const bf16x8*)(As + (wm * WTM + 32 * a + lr) * NSK + 16 * ks + 8 * g);
-#pragma unroll
-    for (int b = 0; b < FB; ++b) bv[b] = read_t(Bs, 16 * ks + 8 * g, wn * WTN + 32 * b, lane);
-#pragma unroll
-    for (int a = 0; a < FA; ++a)
-#pragma unroll
-      for (int b = 0; b < FB; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
-  }
+  for (int o = 0; o < NOP; ++o) op[0][o] = read_op<AT>(As, Bs, 0, o, wm, wn, lane);
+  static_for<0, NM>([&](auto mi) __attribute__((always_inline)) {
+    constexpr int m = decltype(mi)::value;
+    constexpr int ks = m / (FA * FB), idx = m % (FA * FB);
+    constexpr int a = idx / FB, b = idx % FB;
+    __builtin_amdgcn_sched_barrier(0);
+    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[ks & 1][a], op[ks & 1][FA + b],
+                                                        acc[a][b], 0, 0, 0);
+    if constexpr (ks + 1 < KSN && idx < NOP)
+      op[(ks + 1) & 1][idx] = read_op<AT>(As, Bs, ks + 1, idx, wm, wn, lane);
+    if constexpr (WR && m < NCH) write(m);
+    if constexpr (LD && m >= NM - NCH) load(m - (NM - NCH));
+  });
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Write a 256 x 256 fp32 tile: C rows m (out row m0 + m), columns n (n0 + n);
@@ -116,27 +142,21 @@ __global__ __launch_bounds__(NT) void gemm_dw_kernel(GradParams p) {
   const bf16* gsrc = p.g[proj] + hh * p.gs[proj][1] + dd;
   const int64_t gss = p.gs[proj][2];
   const bf16* ysrc = p.y + e0 + 8 * c;
-  u32x4 sa[4], sb[4];
-  auto load = [&](int64_t k0) {  // k0: first flat row (b*S + s) of the stage
+  u32x4 st[NCH];  // chunks 0..3: dK/dV rows, 4..7: y rows
+  const bf16* ga = nullptr;  // first row of the stage being loaded, per operand
+  const bf16* yb = nullptr;
+  auto aim = [&](int64_t k0) {  // k0: first flat row (b*S + s) of a stage
     const int64_t b = k0 / p.S, s0 = k0 % p.S;
-    const bf16* ga = gsrc + b * p.gs[proj][0] + s0 * gss;
-    const bf16* yb = ysrc + k0 * p.E;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = r0 + 16 * i;
-      sa[i] = *(const u32x4*)(ga + r * gss);
-      sb[i] = *(const u32x4*)(yb + (int64_t)r * p.E);
-    }
+    ga = gsrc + b * p.gs[proj][0] + s0 * gss;
+    yb = ysrc + k0 * p.E;
   };
-  auto store = [&](int buf) {
-    bf16* As = smem + buf * 2 * T_EL;
-    bf16* Bs = As + T_EL;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = r0 + 16 * i;
-      *(u32x4*)(As + r * TSK + 8 * c) = sa[i];
-      *(u32x4*)(Bs + r * TSK + 8 * c) = sb[i];
-    }
+  auto load1 = [&](int i) __attribute__((always_inline)) {
+    const int r = r0 + 16 * (i & 3);
+    st[i] = i < 4 ? *(const u32x4*)(ga + r * gss) : *(const u32x4*)(yb + (int64_t)r * p.E);
+  };
+  auto store1 = [&](int i, int buf) __attribute__((always_inline)) {
+    bf16* At = smem + buf * 2 * T_EL + (i < 4 ? 0 : T_EL);
+    *(u32x4*)(At + (r0 + 16 * (i & 3)) * TSK + 8 * c) = st[i];
   };
 
   f32x16 acc[FA][FB];
@@ -145,19 +165,38 @@ __global__ __launch_bounds__(NT) void gemm_dw_kernel(GradParams p) {
 #pragma unroll
     for (int b = 0; b < FB; ++b) acc[a][b] = f32x16{};
   const int64_t nk = (int64_t)p.B * p.S / TK;
-  load(0);
-  store(0);
+  // prologue: stage 0 in buffer 0, stage 1 in flight
+  aim(0);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) load1(i);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) store1(i, 0);
+  if (nk > 1) {
+    aim(TK);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) load1(i);
+  }
   __syncthreads();
-  int buf = 0;
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) load((kt + 1) * TK);
+  int64_t kt = 0;
+  for (; kt + 2 < nk; ++kt) {
+    const int buf = (int)(kt & 1);
     const bf16* As = smem + buf * 2 * T_EL;
-    mma_stage(As, true, As + T_EL, wm, wn, lane, acc);
-    if (!more) break;
-    store(buf ^ 1);
+    aim((kt + 2) * TK);
+    mma_stage<true, true, true>(As, As + T_EL, wm, wn, lane, acc,
+                                [&](int i) { store1(i, buf ^ 1); }, load1);
     __syncthreads();
-    buf ^= 1;
+  }
+  if (kt + 1 < nk) {
+    const int buf = (int)(kt & 1);
+    const bf16* As = smem + buf * 2 * T_EL;
+    mma_stage<true, true, false>(As, As + T_EL, wm, wn, lane, acc,
+                                 [&](int i) { store1(i, buf ^ 1); }, load1);
+    __syncthreads();
+    ++kt;
+  }
+  {
+    const bf16* As = smem + (int)(kt & 1) * 2 * T_EL;
+    mma_stage<true, false, false>(As, As + T_EL, wm, wn, lane, acc, load1, load1);
   }
   store_tile(p.dwt[proj], p.E, n0, p.HD, e0, wm, wn, lane, p.accumulate != 0, acc);
 }
@@ -186,25 +225,23 @@ __global__ __launch_bounds__(NT) void gemm_dy_kernel(GradParams p) {
   }
   // B staging ([k][e], W^T rows): thread covers rows rb + 16 i, chunk cb
   const int cb = tid % 32, rb = tid / 32;
-  u32x4 sa[4], sb[4];
-  auto load = [&](int kt) {  // kt: stage index over K = 2*HD
+  u32x4 st[NCH];  // chunks 0..3: dK/dV rows ([m][k]), 4..7: W^T rows ([k][e])
+  const bf16* gb = nullptr;  // stage bases of the operands being loaded
+  const bf16* wb = nullptr;
+  auto aim = [&](int kt) {  // kt: stage index over K = 2*HD
     const int kk = kt * TK, proj = kk / p.HD, n = kk % p.HD;
     const int hh = n / p.D, dd = n % p.D;
-    const bf16* g = p.g[proj] + hh * p.gs[proj][1] + dd + ca * 8;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sa[i] = *(const u32x4*)(g + arow[i]);
-    const bf16* w = p.wt[proj] + (int64_t)n * p.E + e0 + 8 * cb;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sb[i] = *(const u32x4*)(w + (int64_t)(rb + 16 * i) * p.E);
+    gb = p.g[proj] + hh * p.gs[proj][1] + dd + ca * 8;
+    wb = p.wt[proj] + (int64_t)n * p.E + e0 + 8 * cb;
   };
-  auto store = [&](int buf) {
+  auto load1 = [&](int i) __attribute__((always_inline)) {
+    st[i] = i < 4 ? *(const u32x4*)(gb + arow[i & 3])
+                  : *(const u32x4*)(wb + (int64_t)(rb + 16 * (i & 3)) * p.E);
+  };
+  auto store1 = [&](int i, int buf) __attribute__((always_inline)) {
     bf16* As = smem + buf * (N_EL + T_EL);
-    bf16* Bs = As + N_EL;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *(u32x4*)(As + (ra + 64 * i) * NSK + ca * 8) = sa[i];
-      *(u32x4*)(Bs + (rb + 16 * i) * TSK + 8 * cb) = sb[i];
-    }
+    if (i < 4) *(u32x4*)(As + (ra + 64 * i) * NSK + ca * 8) = st[i];
+    else *(u32x4*)(As + N_EL + (rb + 16 * (i & 3)) * TSK + 8 * cb) = st[i];
   };
 
   f32x16 acc[FA][FB];
@@ -213,19 +250,37 @@ __global__ __launch_bounds__(NT) void gemm_dy_kernel(GradParams p) {
 #pragma unroll
     for (int b = 0; b < FB; ++b) acc[a][b] = f32x16{};
   const int nk = 2 * p.HD / TK;
-  load(0);
-  store(0);
+  aim(0);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) load1(i);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) store1(i, 0);
+  if (nk > 1) {
+    aim(1);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) load1(i);
+  }
   __syncthreads();
-  int buf = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) load(kt + 1);
+  int kt = 0;
+  for (; kt + 2 < nk; ++kt) {
+    const int buf = kt & 1;
     const bf16* As = smem + buf * (N_EL + T_EL);
-    mma_stage(As, false, As + N_EL, wm, wn, lane, acc);
-    if (!more) break;
-    store(buf ^ 1);
+    aim(kt + 2);
+    mma_stage<false, true, true>(As, As + N_EL, wm, wn, lane, acc,
+                                 [&](int i) { store1(i, buf ^ 1); }, load1);
     __syncthreads();
-    buf ^= 1;
+  }
+  if (kt + 1 < nk) {
+    const int buf = kt & 1;
+    const bf16* As = smem + buf * (N_EL + T_EL);
+    mma_stage<false, true, false>(As, As + N_EL, wm, wn, lane, acc,
+                                  [&](int i) { store1(i, buf ^ 1); }, load1);
+    __syncthreads();
+    ++kt;
+  }
+  {
+    const bf16* As = smem + (kt & 1) * (N_EL + T_EL);
+    mma_stage<false, false, false>(As, As + N_EL, wm, wn, lane, acc, load1, load1);
   }
   store_tile(p.dy, p.E, m0, M, e0, wm, wn, lane, p.accumulate != 0, acc);
 }
