@@ -344,11 +344,46 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
 }
 
 // ---------------------------------------------------------------- dQ (Q-stationary)
+//
+// 256 query rows per workgroup, 8 waves of 32 rows, 64-key tiles, arranged
+// like the forward kernel: waves 0-3 (group A) and 4-7 (group B) share the
+// four SIMDs and run one phase apart, so that between two barriers one wave
+// of every SIMD issues MFMAs while the other issues VALU work.  Per tile t a
+// wave runs an MFMA phase
+//   dQ^T += K^T dS^T (tile t-1),  S^T = K Q^T and dP^T = V dO^T (tile t)
+// (48 MFMAs) and a VALU phase  dS^T = P o (dP^T - Delta),
+// P = exp2(S^T * scale*log2(e) - LSE*log2(e)),  plus its share of staging.
+// Slots (barrier intervals) from 0; group A runs
+//   slot 0: S/dP(0);  slot 2t+1: dS(t), write K(t+1);  slot 2t+2: dQ(t), S/dP(t+1)
+// and group B the same one slot later, except that it writes V(t+2) in its
+// VALU slot 2t+2 (V(1) in slot 0), so a tile's V is visible one slot before
+// group A's S/dP of that tile.  Tiles rotate through three LDS buffers; each
+// half of a buffer is rewritten only after its last reader's slot.  Tile rows
+// are laid out in groups of four: rows of a group 320 bytes apart (64 mod 256)
+// and groups 1232 bytes apart (16 mod 64).  Sixteen consecutive rows then
+// start in sixteen distinct 16-byte bank slots (row reads of S and dP by
+// ds_read_b128, one row per lane), and four rows of a group cover all 64
+// banks with 64 bytes each (transposing reads of K^T by ds_read_b64_tr_b16),
+// while every address stays a lane base plus a constant.
+
+template <typename T>
+__device__ inline void hold(T& x) {  // materialise x here: an empty asm that reads and writes it
+  asm volatile("" : "+v"(x));
+}
+
+// Row r of a dQ-kernel tile starts at element rbase(r) (see above).
+constexpr int kRowStr = D + 32, kGrpStr = 3 * kRowStr + D + 8;
+__device__ inline int rbase(int r) { return (r >> 2) * kGrpStr + (r & 3) * kRowStr; }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdParams p) {
-  constexpr int NW = kDqWaves, BN = 32, BM = 32 * NW;
-  constexpr int RM = BN * KSTR, TR = BN * D;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * (2 * RM + TR)];
+  constexpr int BM = 32 * kDqWaves, BN = 64, GT = 64 * kDqWaves / 2;
+  constexpr int TILE = BN / 4 * kGrpStr, STAGE = 2 * TILE, NBUF = 3;
+  constexpr int KC = (BN * D / 8) / GT;  // 16-byte chunks per staging thread and tile
+  static_assert(KC * GT == BN * D / 8, "staging must divide evenly");
+  __shared__ __attribute__((aligned(16))) bf16 smem[NBUF * STAGE];
 
   int g_, t_;
   if (!xcd_group_tile(blockIdx.x, p.tiles, p.groups, &g_, &t_)) return;
@@ -371,7 +406,10 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdParams p) {
   const int64_t r1 = min(qe, r0 + BM);
   if (r0 >= r1) return;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool groupB = wave >= kDqWaves / 2;
+  const int gtid = tid & (GT - 1);
   const int b = bh / p.H, h = bh % p.H;
   const int64_t wrow0 = r0 + wave * 32;
   const int64_t myrow = wrow0 + lr;
@@ -392,116 +430,228 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdParams p) {
   float lse2 = INFINITY, dlt = 0.f;
   if (row_ok) {
     float l = p.lse[(int64_t)bh * p.SQ + myrow];
-    lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+    lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;  // +inf: the row takes no weight
     dlt = p.delta[(int64_t)bh * p.SQ + myrow];
   }
   f32x16 dq[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) dq[dt] = f32x16{};
 
-  int r = 0;
-  int64_t kc = 0, kend = 0;
-  auto seg = [&](int rr, int64_t* a, int64_t* e) {
-    int kb = fixed_kb >= 0 ? fixed_kb : shard_at_step(p.sched, p.n, j, rr);
-    *a = shard_start(p.SKV, p.n, kb);
-    *e = shard_start(p.SKV, p.n, kb + 1);
-    if (p.causal && *e > r1) *e = r1;
-    if (*e < *a) *e = *a;
+  // key tiles over the ordered segments
+  struct It {
+    int r;
+    int64_t kt, ke;
   };
-  auto seek = [&](int from) {
-    for (r = from; r < nseg; ++r) {
-      int64_t a, e;
-      seg(r, &a, &e);
-      if (e > a) { kc = a; kend = e; return; }
+  auto seek = [&](It& it, int from) {
+    for (it.r = from; it.r < nseg; ++it.r) {
+      int kb = fixed_kb >= 0 ? fixed_kb : shard_at_step(p.sched, p.n, j, it.r);
+      int64_t a = shard_start(p.SKV, p.n, kb), e = shard_start(p.SKV, p.n, kb + 1);
+      if (p.causal && e > r1) e = r1;
+      if (e > a) {
+        it.kt = a;
+        it.ke = e;
+        return;
+      }
     }
+    it.kt = it.ke = 0;
   };
-  seek(0);
-  if (r >= nseg && acc_in) return;
+  auto advance = [&](It& it) {
+    it.kt += BN;
+    if (it.kt >= it.ke) seek(it, it.r + 1);
+  };
+  It tv;  // tile of the next VALU phase
+  seek(tv, 0);
+  if (tv.r >= nseg && acc_in) return;  // nothing to add this round
 
-  u32x4 stg[4];
-  auto load = [&](int64_t k0, int64_t k1) {
-    if (tid >= 256) return;  // 256 staging threads: K rows, then V rows
-    if (tid < 128) {
-      const int quad = tid / 16, col8 = tid % 16;
+  // staging: group A moves K tiles, group B V tiles; thread chunks are rows
+  // srow0 + 16 i of a tile at chunk column scol
+  const bf16* ssrc = groupB ? vg : kg;
+  const int64_t sstr = groupB ? p.sv[2] : p.sk[2];
+  const int soff = groupB ? TILE : 0;
+  const int srow0 = gtid / (D / 8), scol = gtid % (D / 8);
+  constexpr int srstep = GT / (D / 8);
+  u32x4 stg[KC];
+  // Rows at or past the segment end repeat its last key (masked below).  Row
+  // strides are below 16 MiB (checked on the host), so a chunk's byte offset
+  // from the tile's first row is a 24-bit product.
+  const uint32_t sstr2 = (uint32_t)(sstr * 2);
+  auto load_tile = [&](const It& t) {
+    const int lim = (int)min(t.ke - t.kt, (int64_t)BN);
+    const char* base = (const char*)(ssrc + t.kt * sstr);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        int64_t key = k0 + 4 * quad + rr;
-        stg[rr] = key < k1 ? *(const u32x4*)(kg + key * p.sk[2] + col8 * 8) : u32x4{};
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = (tid - 128) + i * 128;
-        const int row = c / 16, col8 = c % 16;
-        int64_t key = k0 + row;
-        stg[i] = key < k1 ? *(const u32x4*)(vg + key * p.sv[2] + col8 * 8) : u32x4{};
-      }
+    for (int i = 0; i < KC; ++i) {
+      const int r = min(srow0 + i * srstep, lim - 1);
+      const uint32_t off = __umul24((uint32_t)r, sstr2) + (uint32_t)(scol * 16);
+      stg[i] = *(const u32x4*)(base + off);
     }
   };
-  auto store = [&](int buf) {
-    if (tid >= 256) return;
-    bf16* base = smem + buf * (2 * RM + TR);
-    if (tid < 128) {
-      put_rows(base, base + 2 * RM, tid / 16, tid % 16, stg);
-    } else {
+  static_assert(srstep % 4 == 0, "staging rows keep their place in a row group");
+  const int wbase = soff + rbase(srow0) + scol * 8;
+  auto store_tile = [&](int buf) {
+    bf16* dst = smem + buf * STAGE + wbase;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = (tid - 128) + i * 128;
-        *(u32x4*)(base + RM + (c / 16) * KSTR + (c % 16) * 8) = stg[i];
-      }
-    }
+    for (int i = 0; i < KC; ++i) *(u32x4*)(dst + i * (srstep / 4) * kGrpStr) = stg[i];
   };
 
-  int buf = 0;
-  if (r < nseg) { load(kc, kend); store(0); }
-  __syncthreads();
+  f32x16 sacc[BN / 32], pacc[BN / 32];
+  bf16x8 dsb[BN / 16];
+  // S^T = K Q^T and dP^T = V dO^T; element 4i+jj of block u is key 32u+8i+4g+jj
+  const int rb = rbase(lr) + 8 * g;  // this lane's row-read base
+  auto phase_sdp = [&](int buf) {
+    const bf16* ks = smem + buf * STAGE + rb;
+    const bf16* vs = ks + TILE;
+#pragma unroll
+    for (int u = 0; u < BN / 32; ++u) sacc[u] = pacc[u] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+      for (int u = 0; u < BN / 32; ++u) {
+        const int off = u * 8 * kGrpStr + 16 * s;  // row 32u + lr, columns 16s + 8g ..
+        sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(ks + off), qreg[s],
+                                                          sacc[u], 0, 0, 0);
+        pacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vs + off), doreg[s],
+                                                          pacc[u], 0, 0, 0);
+      }
+  };
+  // dQ^T += K^T dS^T: the A operand of step t covers keys 16t+4g+{0..3} and
+  // 16t+4g+8+{0..3} of head dims 32dt + lane%32, the key order of dsb[t]; lane
+  // address: row 16t + 4g + li/4 (group 4t + g), column 32dt + 16*(lane/16 % 2) + 4*(li % 4)
+  const int li = lane & 15;
+  const int tb = g * kGrpStr + (li >> 2) * kRowStr + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
+  // One MFMA slot as a fixed sequence: dQ of the current tile (16 MFMAs), then
+  // S and dP of the next (32).  The A operand of MFMA m + DIST is read from
+  // LDS just before MFMA m is issued and a scheduling barrier follows every
+  // MFMA, so each read has DIST MFMAs to arrive.
+  constexpr int NDQ = (BN / 16) * (D / 32), NSP = 2 * (D / 16) * (BN / 32), NM = NDQ + NSP;
+  constexpr int DIST = 2, NB = DIST + 1;
+  auto op_read = [&](auto M, int cur_buf, int nxt_buf) -> bf16x8 {
+    constexpr int m = decltype(M)::value;
+    if constexpr (m < NDQ) {
+      constexpr int t = m / (D / 32), dt = m % (D / 32);
+      const bf16* a0 = smem + cur_buf * STAGE + tb + 4 * t * kGrpStr + 32 * dt;
+      s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
+      s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0 + 2 * kGrpStr));
+      u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+    } else {
+      constexpr int q = m - NDQ, s = q / 4, u = (q / 2) % 2, kind = q % 2;
+      return *(const bf16x8*)(smem + nxt_buf * STAGE + kind * TILE + rb + u * 8 * kGrpStr + 16 * s);
+    }
+  };
+  auto op_mfma = [&](auto M, const bf16x8& a) {
+    constexpr int m = decltype(M)::value;
+    if constexpr (m < NDQ) {
+      constexpr int t = m / (D / 32), dt = m % (D / 32);
+      dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb[t], dq[dt], 0, 0, 0);
+    } else {
+      constexpr int q = m - NDQ, s = q / 4, u = (q / 2) % 2, kind = q % 2;
+      if constexpr (kind == 0)
+        sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], s == 0 ? f32x16{} : sacc[u],
+                                                          0, 0, 0);
+      else
+        pacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, doreg[s], s == 0 ? f32x16{} : pacc[u],
+                                                          0, 0, 0);
+    }
+  };
+  auto mfma_slot = [&](int cur_buf, int nxt_buf) {
+    bf16x8 ob[NB];
+    static_for<0, DIST>([&](auto M) { ob[decltype(M)::value % NB] = op_read(M, cur_buf, nxt_buf); });
+    static_for<0, NM>([&](auto M) {
+      constexpr int m = decltype(M)::value;
+      if constexpr (m + DIST < NM)
+        ob[(m + DIST) % NB] = op_read(std::integral_constant<int, m + DIST>{}, cur_buf, nxt_buf);
+      op_mfma(M, ob[m % NB]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
   const float c2 = p.scale_log2;
-  while (r < nseg) {
-    const int64_t k0 = kc, k1 = kend;
-    int64_t nk0 = 0, nk1 = 0;
-    bool more;
-    {
-      int64_t nx = kc + BN;
-      if (nx < kend) { more = true; nk0 = nx; nk1 = kend; kc = nx; }
-      else { seek(r + 1); more = r < nseg; nk0 = kc; nk1 = kend; }
+  auto phase_ds = [&](const It& t) {
+    const bool need_mask = (t.kt + BN > t.ke) || (p.causal && t.kt + BN - 1 > wrow0);
+    int lim = BN;  // this row sees keys kt .. kt+lim-1 of the tile
+    if (need_mask) {
+      int64_t l = min(t.ke - t.kt, (int64_t)BN);
+      if (p.causal && myrow + 1 - t.kt < l) l = myrow + 1 - t.kt;
+      lim = (int)max(l, (int64_t)0);
     }
-    if (more) load(nk0, nk1);
+#pragma unroll
+    for (int u = 0; u < BN / 32; ++u)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        bf16x8 x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int idx = 8 * hh + e;
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[u][idx], c2, -lse2));
+          if (need_mask && 32 * u + 8 * (idx / 4) + 4 * g + (idx % 4) >= lim) pv = 0.f;
+          x[e] = (bf16)(pv * (pacc[u][idx] - dlt));  // dS^T (unscaled)
+        }
+        dsb[2 * u + hh] = x;
+      }
+  };
 
-    const bf16* base = smem + buf * (2 * RM + TR);
-    const bf16* Ks = base;
-    const bf16* Vs = base + RM;
-    const bf16* Kt = base + 2 * RM;
-    f32x16 sacc = f32x16{}, pacc = f32x16{};
+  // ---- prologue: tile 0 in buffer 0, each group's next tile in flight
+  // (a job without key tiles skips all of it, so both groups meet the same barriers)
+  It tw = tv;  // next tile this thread's group stages
+  if (tv.r < nseg) {
+    load_tile(tw);
+    store_tile(0);
+    advance(tw);
+    if (tw.r < nseg) load_tile(tw);
+    __syncthreads();
+    if (!groupB) {
+      phase_sdp(0);  // slot 0
+    } else {
+      if (tw.r < nseg) {  // slot 0: V(1)
+        store_tile(1);
+        advance(tw);
+        if (tw.r < nseg) load_tile(tw);
+      }
+      __syncthreads();
+      phase_sdp(0);  // slot 1
+    }
+#pragma unroll
+    for (int u = 0; u < BN / 32; ++u) {
+      hold(sacc[u]);
+      hold(pacc[u]);
+    }
+    __syncthreads();
+    // settle the prologue's global loads here, not inside the loop
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      bf16x8 ak = *(const bf16x8*)(Ks + lr * KSTR + 16 * s + 8 * g);
-      bf16x8 av = *(const bf16x8*)(Vs + lr * KSTR + 16 * s + 8 * g);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[s], sacc, 0, 0, 0);
-      pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, doreg[s], pacc, 0, 0, 0);
+      hold(qreg[s]);
+      hold(doreg[s]);
     }
-    // element 4i+jj is key k0 + 8i + 4g + jj; this lane's query is myrow
-    const bool need_mask = (k0 + BN > k1) || (p.causal && k0 + BN - 1 > wrow0);
+    hold(lse2);
+    hold(dlt);
+    int it = 0;
+    while (tv.r < nseg) {
+      const int cur = it % 3;
+      // Staged chunks go to LDS first, so that their registers are free during
+      // dS; the next tile's loads are issued last and have the following MFMA
+      // slot to land.
+      const bool stage = tw.r < nseg;  // group A: K(it+1); group B: V(it+2)
+      if (stage) store_tile(groupB ? (it + 2) % 3 : (it + 1) % 3);
+      phase_ds(tv);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], c2, -lse2));
-      if (need_mask) {
-        int64_t key = k0 + 8 * (e / 4) + 4 * g + (e % 4);
-        if (key >= k1 || (p.causal && key > myrow)) pv = 0.f;
+      for (int t = 0; t < BN / 16; ++t) hold(dsb[t]);
+      if (stage) {
+        advance(tw);
+        if (tw.r < nseg) load_tile(tw);
       }
-      pacc[e] = pv * (pacc[e] - dlt);  // dS^T (unscaled)
-    }
+      __syncthreads();
+      It tn = tv;
+      advance(tn);
+      mfma_slot(cur, (it + 1) % 3);  // after the last tile S/dP read a stale buffer, unused
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      bf16x8 sb = pack8(pacc, hh);
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(Kt, hh, dt, lr, g), sb, dq[dt],
-                                                         0, 0, 0);
+      for (int u = 0; u < BN / 32; ++u) {
+        hold(sacc[u]);
+        hold(pacc[u]);
+      }
+      // group A closes this slot; group B's last MFMA slot is the final one
+      if (!groupB || tn.r < nseg) __syncthreads();
+      tv = tn;
+      ++it;
     }
-    if (!more) break;
-    store(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
   }
 
   if (!row_ok) return;
