@@ -12,9 +12,9 @@
 // registers while query tiles stream past (LV-XAttn: KV stays put, Q/dO/LSE/
 // Delta rotate); the Q-stationary kernel keeps a query tile's Q, dO, dQ in
 // registers while key tiles stream past (Ring Attention).  Every contraction
-// is a v_mfma_f32_32x32x16_bf16; operands whose contraction index is the
-// row index of their storage (dO^T, Q^T, K^T) are staged in LDS as
-// [row/4][d][4] so that four consecutive rows of one column are 8 bytes.
+// is a v_mfma_f32_32x32x16_bf16; operands whose contraction index is the row
+// index of their storage (dO^T, Q^T, K^T) are read from the row-major LDS
+// tiles with the transposing ds_read_b64_tr_b16.
 #include <type_traits>
 
 #include "bwd_args.h"
@@ -40,45 +40,10 @@ struct BwdParams {
 namespace {
 
 constexpr int D = 128;
-constexpr int KSTR = D + 8;  // row-major LDS row stride (elements)
-
-__device__ inline float swap32_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 __device__ inline uint32_t pk_bf16(float a, float b) {
   bf16 x = (bf16)a, y = (bf16)b;
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
-}
-
-// Write a staged 4-row x 8-column block (r[0..3], 16 bytes each) into LDS,
-// row-major at rm (row stride KSTR) and/or as [row/4][d][4] at tr.
-__device__ inline void put_rows(bf16* rm, bf16* tr, int quad, int col8, const u32x4* r) {
-  if (rm) {
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) *(u32x4*)(rm + (4 * quad + rr) * KSTR + col8 * 8) = r[rr];
-  }
-  if (tr) {
-    bf16* dst = tr + (quad * D + col8 * 8) * 4;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t lo01 = (r[0][w] & 0xffffu) | (r[1][w] << 16);
-      uint32_t lo23 = (r[2][w] & 0xffffu) | (r[3][w] << 16);
-      uint32_t hi01 = (r[0][w] >> 16) | (r[1][w] & 0xffff0000u);
-      uint32_t hi23 = (r[2][w] >> 16) | (r[3][w] & 0xffff0000u);
-      *(u32x4*)(dst + 8 * w) = u32x4{lo01, lo23, hi01, hi23};
-    }
-  }
-}
-
-// A operand (rows d = 32*dt + lane%32, 16 contraction rows of step t) from a
-// [row/4][d][4] LDS tile.
-__device__ inline bf16x8 tr_operand(const bf16* tr, int t, int dt, int lr, int g) {
-  const int d = 32 * dt + lr;
-  u32x2 lo = *(const u32x2*)(tr + ((4 * t + g) * D + d) * 4);
-  u32x2 hi = *(const u32x2*)(tr + ((4 * t + 2 + g) * D + d) * 4);
-  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
 __device__ inline bf16x8 pack8(const f32x16& c, int h) {
@@ -125,23 +90,67 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
   if (row < rows && c == 0) p.delta[row] = s;
 }
 
+// LDS tiles of the two MFMA kernels below keep their rows in groups of four:
+// rows of a group 320 bytes apart (64 mod 256) and groups 1232 bytes apart
+// (16 mod 64).  Sixteen consecutive rows then start in sixteen distinct
+// 16-byte bank slots (row reads by ds_read_b128, one row per lane), and four
+// rows of a group cover all 64 banks with 64 bytes each (transposing reads by
+// ds_read_b64_tr_b16), while every address stays a lane base plus a constant.
+constexpr int kRowStr = D + 32, kGrpStr = 3 * kRowStr + D + 8;
+__device__ inline int rbase(int r) { return (r >> 2) * kGrpStr + (r & 3) * kRowStr; }
+
+template <typename T>
+__device__ inline void hold(T& x) {  // materialise x here: an empty asm that reads and writes it
+  asm volatile("" : "+v"(x));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// A operand of 16 contraction rows (16t + 4g + {0..3}, 16t + 4g + 8 + {0..3};
+// the row order of an MFMA result packed by pack8) x head dims 32dt + lane%32,
+// read transposed from a row-major tile whose lane base is trb (below).
+__device__ inline bf16x8 tr_rows(const bf16* tile_lane, int t, int dt) {
+  const bf16* a0 = tile_lane + 4 * t * kGrpStr + 32 * dt;
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0 + 2 * kGrpStr));
+  u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+}
+// Lane base of tr_rows: row 4g + li/4 (li = lane % 16), column 16*(lane/16 % 2) + 4*(li % 4).
+__device__ inline int trb(int lane) {
+  const int li = lane & 15, g = lane >> 5;
+  return g * kGrpStr + (li >> 2) * kRowStr + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
+}
+
 // ---------------------------------------------------------------- dK, dV (KV-stationary)
 //
-// 128 keys per workgroup, 8 waves: waves 0-3 compute dV and waves 4-7 dK for
-// the same four 32-key groups (wave w and w+4 share a SIMD).  Splitting by
-// output keeps each wave under half the register file (dV: K and dV; dK: K, V
-// and dK), so two waves run per SIMD; the price is that S is computed by both
-// roles (40 instead of 32 MFMAs per 32 x 32 block).  Queries stream in steps
-// of 64 rows, staged by the dV waves.
+// 128 keys per workgroup; 8 waves in two roles over the same four 32-key
+// groups: waves 0-3 (group A) accumulate dV, waves 4-7 (group B) dK, and wave
+// w shares its SIMD with wave w+4.  Splitting by output keeps each wave within
+// half the register file (A holds K and dV, B holds K, V and dK); the price is
+// that S is computed by both roles.  Queries stream in tiles of 64 rows, and
+// the two groups alternate like the dQ kernel's, one phase apart:
+//   A: MFMA  dV^T += dO^T P (tile j-1), S = Q K^T (tile j)            32 MFMAs
+//      VALU  P = exp2(S scale log2(e) - LSE log2(e)), writes Q(j+1), LSE, Delta
+//   B: MFMA  dK^T += Q^T dS (tile j-1), S and dP = dO V^T (tile j)    48 MFMAs
+//      VALU  dS = P o (dP - Delta), writes dO(j+1)
+// Slots from 0:  A: slot 0: S(0);  2j+1: P(j);  2j+2: dV(j), S(j+1)
+//                B: slot 1: S/dP(0);  2j+2: dS(j);  2j+3: dK(j), S/dP(j+1)
+// Q tiles (with their rows' LSE and Delta) and dO tiles rotate through three
+// LDS buffers; Q(j) is read from slot 2j to 2j+3 and rewritten (as Q(j+3)) in
+// slot 2j+5, dO(j) is read in slots 2j+1 and 2j+2 and rewritten in slot 2j+6.
 
 // dK/dV: 8 waves in two roles; dQ: 8 waves, two per SIMD.
 constexpr int kDkdvWaves = 8, kDqWaves = 8;
 
 __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) {
-  constexpr int BQ = 64, BK = 128;
-  constexpr int RM = BQ * KSTR, TR = BQ * D;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * (2 * RM + 2 * TR)];
-  __shared__ float s_lse[2][BQ], s_dlt[2][BQ];
+  constexpr int BK = 128, BQ = 64, GT = 64 * kDkdvWaves / 2;
+  constexpr int TILE = BQ / 4 * kGrpStr, STAGE = 2 * TILE, NBUF = 3;
+  constexpr int KC = (BQ * D / 8) / GT;  // 16-byte chunks per staging thread and tile
+  static_assert(KC * GT == BQ * D / 8, "staging must divide evenly");
+  __shared__ __attribute__((aligned(16))) bf16 smem[NBUF * STAGE];
+  __shared__ float s_lse[NBUF][BQ], s_dlt[NBUF][BQ];
 
   int g_, t_;
   if (!xcd_group_tile(blockIdx.x, p.tiles, p.groups, &g_, &t_)) return;
@@ -164,7 +173,10 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
   const int64_t kt1 = min(ke, kt0 + BK);
   if (kt0 >= kt1) return;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool groupB = wave >= kDkdvWaves / 2;  // B: dK, A: dV
+  const int gtid = tid & (GT - 1);
   const int b = bh / p.H, h = bh % p.H;
   const int64_t kw0 = kt0 + (wave & 3) * 32;
   const int64_t mykey = kw0 + lr;
@@ -175,172 +187,289 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
   const float* lseg = p.lse + (int64_t)bh * p.SQ;
   const float* dltg = p.delta + (int64_t)bh * p.SQ;
 
-  // q-step iterator over the ordered segments
-  int r = 0;
-  int64_t qc = 0, qend = 0;
-  auto seg = [&](int rr, int64_t* a, int64_t* e) {
-    int qb = fixed_qb >= 0 ? fixed_qb : qblock_at_step(p.sched, p.n, shard, rr);
-    *a = shard_start(p.SQ, p.n, qb);
-    *e = shard_start(p.SQ, p.n, qb + 1);
-    if (p.causal && *a < kt0) *a = kt0;  // queries before the tile's first key see none of it
-    if (*e < *a) *e = *a;
-  };
-  auto seek = [&](int from) {
-    for (r = from; r < nseg; ++r) {
-      int64_t a, e;
-      seg(r, &a, &e);
-      if (e > a) { qc = a; qend = e; return; }
+  // K (both roles) and V (dK role) rows of this lane's key, as B operands
+  bf16x8 kreg[D / 16], vreg[D / 16];
+  {
+    const bf16* kp = p.k + b * p.sk[0] + h * p.sk[1] + mykey * p.sk[2];
+    const bf16* vp = p.v + b * p.sv[0] + h * p.sv[1] + mykey * p.sv[2];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      kreg[s] = key_ok ? *(const bf16x8*)(kp + 16 * s + 8 * g) : bf16x8{};
+      vreg[s] = (key_ok && groupB) ? *(const bf16x8*)(vp + 16 * s + 8 * g) : bf16x8{};
     }
-  };
-  seek(0);
-  if (r >= nseg && acc_in) return;  // nothing to add this round
+  }
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
 
-  // staging by the dV waves (threads 0-255): each moves the same 4-row x
-  // 8-column block of Q and of dO
-  u32x4 stg[8];
+  // query tiles over the ordered segments
+  struct It {
+    int r;
+    int64_t qt, qe;
+  };
+  auto seek = [&](It& it, int from) {
+    for (it.r = from; it.r < nseg; ++it.r) {
+      int qb = fixed_qb >= 0 ? fixed_qb : qblock_at_step(p.sched, p.n, shard, it.r);
+      int64_t a = shard_start(p.SQ, p.n, qb), e = shard_start(p.SQ, p.n, qb + 1);
+      if (p.causal && a < kt0) a = kt0;  // queries before the tile's first key see none of it
+      if (e > a) {
+        it.qt = a;
+        it.qe = e;
+        return;
+      }
+    }
+    it.qt = it.qe = 0;
+  };
+  auto advance = [&](It& it) {
+    it.qt += BQ;
+    if (it.qt >= it.qe) seek(it, it.r + 1);
+  };
+  It tv;  // tile of the next VALU phase
+  seek(tv, 0);
+  if (tv.r >= nseg && acc_in) return;  // nothing to add this round
+
+  // staging: group A moves Q tiles (and the rows' LSE, Delta), group B dO
+  // tiles; thread chunks are rows srow0 + 16 i of a tile at chunk column scol
+  const bf16* ssrc = groupB ? dog : qg;
+  const int64_t sstr = groupB ? p.sdo[2] : p.sq[2];
+  const int soff = groupB ? TILE : 0;
+  const int srow0 = gtid / (D / 8), scol = gtid % (D / 8);
+  constexpr int srstep = GT / (D / 8);
+  static_assert(srstep % 4 == 0, "staging rows keep their place in a row group");
+  u32x4 stg[KC];
+  // Per query row of a tile, LDS holds the seeds of its S and dP accumulators,
+  // -LSE/scale and -Delta, so that the MFMAs produce S - LSE/scale (P is
+  // exp2 of it times scale*log2(e)) and dP - Delta without VALU work or LDS
+  // reads in the VALU phase.
   float st_l = 0.f, st_d = 0.f;
-  auto load = [&](int64_t q0, int64_t q1) {
-    if (tid >= 256) return;
-    const int quad = tid / 16, col8 = tid % 16;
+  const float rscale = 1.f / p.scale;
+  // Rows at or past the segment end repeat its last row and get LSE = +inf
+  // (no weight).  Row strides are below 16 MiB (checked on the host), so a
+  // chunk's byte offset from the tile's first row is a 24-bit product.
+  const uint32_t sstr2 = (uint32_t)(sstr * 2);
+  auto load_tile = [&](const It& t) {
+    const int lim = (int)min(t.qe - t.qt, (int64_t)BQ);
+    const char* base = (const char*)(ssrc + t.qt * sstr);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int64_t row = q0 + 4 * quad + rr;
-      const bool ok = row < q1;
-      stg[rr] = ok ? *(const u32x4*)(qg + row * p.sq[2] + col8 * 8) : u32x4{};
-      stg[4 + rr] = ok ? *(const u32x4*)(dog + row * p.sdo[2] + col8 * 8) : u32x4{};
+    for (int i = 0; i < KC; ++i) {
+      const int r = min(srow0 + i * srstep, lim - 1);
+      const uint32_t off = __umul24((uint32_t)r, sstr2) + (uint32_t)(scol * 16);
+      stg[i] = *(const u32x4*)(base + off);
     }
-    if (tid < BQ) {
-      int64_t row = q0 + tid;
-      float l = row < q1 ? lseg[row] : -INFINITY;
-      st_l = (l == -INFINITY) ? INFINITY : l * kLog2e;  // +inf: the row takes no weight
-      st_d = row < q1 ? dltg[row] : 0.f;
+    if (!groupB && gtid < BQ) {
+      const int64_t row = t.qt + gtid;
+      const float l = gtid < lim ? lseg[row] : -INFINITY;
+      st_l = (l == -INFINITY) ? -INFINITY : -l * rscale;  // -inf: the row takes no weight
+      st_d = gtid < lim ? -dltg[row] : 0.f;
     }
   };
-  auto store = [&](int buf) {
-    if (tid >= 256) return;
-    bf16* base = smem + buf * (2 * RM + 2 * TR);
-    const int quad = tid / 16, col8 = tid % 16;
-    put_rows(base, base + 2 * RM, quad, col8, stg);
-    put_rows(base + RM, base + 2 * RM + TR, quad, col8, stg + 4);
-    if (tid < BQ) { s_lse[buf][tid] = st_l; s_dlt[buf][tid] = st_d; }
+  const int wbase = soff + rbase(srow0) + scol * 8;
+  auto store_tile = [&](int buf) {
+    bf16* dst = smem + buf * STAGE + wbase;
+#pragma unroll
+    for (int i = 0; i < KC; ++i) *(u32x4*)(dst + i * (srstep / 4) * kGrpStr) = stg[i];
+    if (!groupB && gtid < BQ) {
+      s_lse[buf][gtid] = st_l;
+      s_dlt[buf][gtid] = st_d;
+    }
   };
 
-  if (r < nseg) { load(qc, qend); store(0); }
-  __syncthreads();
+  f32x16 sacc[BQ / 32], pacc[BQ / 32];
+  bf16x8 xb[BQ / 16];  // P (A) or dS (B) of the last VALU phase, bf16, in MFMA B-operand order
+  const int rb = rbase(lr) + 8 * g;  // this lane's row-read base
+  const int tb = trb(lane);
+  // One MFMA slot as a fixed sequence: dV or dK of the current tile (16
+  // MFMAs), then S (and dP) of the next (16 or 32).  The A operand of MFMA
+  // m + DIST is read from LDS just before MFMA m is issued and a scheduling
+  // barrier follows every MFMA, so each read has DIST MFMAs to arrive.
+  constexpr int NACC = (BQ / 16) * (D / 32), DIST = 2, NOB = DIST + 1, SEED_AHEAD = 4;
+  // S and dP accumulators seeded from LDS; element 4i+jj of block u is query
+  // row 32u + 8i + 4g + jj of the tile
+  auto seed = [&](bool rb_role, int buf) {
+#pragma unroll
+    for (int u = 0; u < BQ / 32; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int qo = 32 * u + 8 * i + 4 * g;
+        const f32x4 l4 = *(const f32x4*)(&s_lse[buf][qo]);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) sacc[u][4 * i + jj] = l4[jj];
+        if (rb_role) {
+          const f32x4 d4 = *(const f32x4*)(&s_dlt[buf][qo]);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) pacc[u][4 * i + jj] = d4[jj];
+        }
+      }
+  };
+  auto mfma_slot = [&](auto ROLE_B, int cur_buf, int nxt_buf) {
+    constexpr bool RB = decltype(ROLE_B)::value;
+    constexpr int NM = NACC + (RB ? 2 : 1) * (D / 16) * (BQ / 32);
+    auto rd = [&](auto M) -> bf16x8 {
+      constexpr int m = decltype(M)::value;
+      if constexpr (m < NACC) {  // dV: dO^T from the dO half; dK: Q^T from the Q half
+        return tr_rows(smem + cur_buf * STAGE + (RB ? 0 : TILE) + tb, m / (D / 32), m % (D / 32));
+      } else {  // S: Q rows; dP: dO rows
+        constexpr int q = m - NACC, per = RB ? 2 : 1;
+        constexpr int s = q / (per * (BQ / 32)), u = (q / per) % (BQ / 32), kind = q % per;
+        return *(const bf16x8*)(smem + nxt_buf * STAGE + kind * TILE + rb + u * 8 * kGrpStr + 16 * s);
+      }
+    };
+    auto mf = [&](auto M, const bf16x8& a) {
+      constexpr int m = decltype(M)::value;
+      if constexpr (m < NACC) {
+        constexpr int t = m / (D / 32), dt = m % (D / 32);
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xb[t], acc[dt], 0, 0, 0);
+      } else {
+        constexpr int q = m - NACC, per = RB ? 2 : 1;
+        constexpr int s = q / (per * (BQ / 32)), u = (q / per) % (BQ / 32), kind = q % per;
+        if constexpr (kind == 0)
+          sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[s], sacc[u], 0, 0, 0);
+        else
+          pacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vreg[s], pacc[u], 0, 0, 0);
+      }
+    };
+    bf16x8 ob[NOB];
+    static_for<0, DIST>([&](auto M) { ob[decltype(M)::value % NOB] = rd(M); });
+    static_for<0, NM>([&](auto M) {
+      constexpr int m = decltype(M)::value;
+      // seeds late in the dV/dK part, when most of xb is dead
+      if constexpr (m == NACC - SEED_AHEAD) seed(RB, nxt_buf);
+      if constexpr (m + DIST < NM) ob[(m + DIST) % NOB] = rd(std::integral_constant<int, m + DIST>{});
+      mf(M, ob[m % NOB]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  // S-only prologue slot (tile 0 in buffer 0)
+  auto first_s = [&](auto ROLE_B) {
+    constexpr bool RB = decltype(ROLE_B)::value;
+    seed(RB, 0);
+    const bf16* qs = smem + rb;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+      for (int u = 0; u < BQ / 32; ++u) {
+        const int off = u * 8 * kGrpStr + 16 * s;
+        sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qs + off), kreg[s],
+                                                          sacc[u], 0, 0, 0);
+        if constexpr (RB)
+          pacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qs + TILE + off),
+                                                            vreg[s], pacc[u], 0, 0, 0);
+      }
+  };
   const float c2 = p.scale_log2;
-
-  // One role's whole loop: IS_DK selects dK (needs V) or dV.
-  auto run = [&](auto role) __attribute__((always_inline)) {
-    constexpr bool IS_DK = decltype(role)::value;
-    bf16x8 kreg[D / 16], vreg[IS_DK ? D / 16 : 1];
-    {
-      const bf16* kp = p.k + b * p.sk[0] + h * p.sk[1] + mykey * p.sk[2];
-      const bf16* vp = p.v + b * p.sv[0] + h * p.sv[1] + mykey * p.sv[2];
+  // P (A) or dS (B) of a tile; element 4i+jj of block u is query qt + 32u + 8i + 4g + jj
+  auto phase_valu = [&](auto ROLE_B, const It& t) {
+    constexpr bool RB = decltype(ROLE_B)::value;
+    const bool need_mask = p.causal && t.qt < kw0 + 31;
+    // query offsets below lim precede this lane's key: no weight
+    const int lim = need_mask ? (int)max(min(mykey - t.qt, (int64_t)BQ), (int64_t)0) : 0;
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        kreg[s] = key_ok ? *(const bf16x8*)(kp + 16 * s + 8 * g) : bf16x8{};
-        if constexpr (IS_DK) vreg[s] = key_ok ? *(const bf16x8*)(vp + 16 * s + 8 * g) : bf16x8{};
+    for (int u = 0; u < BQ / 32; ++u) {  // one 32-query block at a time
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[u][e] = __builtin_amdgcn_exp2f(sacc[u][e] * c2);  // P
+      if (need_mask) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (32 * u + 8 * (e / 4) + 4 * g + (e % 4) < lim) sacc[u][e] = 0.f;
       }
-    }
-    f32x16 acc[D / 32];
+      if constexpr (RB) {
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
-
-    int buf = 0;
-    while (r < nseg) {
-      const int64_t q0 = qc;
-      int64_t nq0 = 0, nq1 = 0;
-      bool more;
-      {
-        int64_t nx = qc + BQ;
-        if (nx < qend) { more = true; nq0 = nx; nq1 = qend; qc = nx; }
-        else { seek(r + 1); more = r < nseg; nq0 = qc; nq1 = qend; }
+        for (int e = 0; e < 16; ++e) sacc[u][e] *= pacc[u][e];  // dS (unscaled)
       }
-      if (!IS_DK && more) load(nq0, nq1);
-
-      const bf16* base = smem + buf * (2 * RM + 2 * TR);
-      const bf16* Qs = base;
-      const bf16* Ds = base + RM;
-      const bf16* Qt = base + 2 * RM;
-      const bf16* Dt = base + 2 * RM + TR;
-
-      // the two 32-query halves one after the other (keeps the live score
-      // tiles to one S and one dP block per wave)
-      const bool need_mask = p.causal && (q0 < kw0 + 31);
-#pragma unroll
-      for (int qh = 0; qh < BQ / 32; ++qh) {
-        f32x16 sacc = f32x16{}, pacc = f32x16{};
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          bf16x8 aq = *(const bf16x8*)(Qs + (32 * qh + lr) * KSTR + 16 * s + 8 * g);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[s], sacc, 0, 0, 0);
-          if constexpr (IS_DK) {
-            bf16x8 ad = *(const bf16x8*)(Ds + (32 * qh + lr) * KSTR + 16 * s + 8 * g);
-            pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vreg[s], pacc, 0, 0, 0);
-          }
-        }
-        // element 4i+j is query q0 + 32qh + 8i + 4g + j; this lane's key is mykey
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int qo = 32 * qh + 8 * i + 4 * g;
-          f32x4 l4 = *(const f32x4*)(&s_lse[buf][qo]);
-          f32x4 d4 = *(const f32x4*)(&s_dlt[buf][qo]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * i + j], c2, -l4[j]));
-            if (need_mask && mykey > q0 + qo + j) pv = 0.f;
-            if constexpr (IS_DK)
-              sacc[4 * i + j] = pv * (pacc[4 * i + j] - d4[j]);  // dS (unscaled)
-            else
-              sacc[4 * i + j] = pv;  // P
-          }
-        }
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const bf16x8 xb = pack8(sacc, hh);
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt)
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                tr_operand(IS_DK ? Qt : Dt, 2 * qh + hh, dt, lr, g), xb, acc[dt], 0, 0, 0);
-        }
-      }
-      if (!more) break;
-      if constexpr (!IS_DK) store(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
-    }
-
-    if (!key_ok) return;
-    const float sc = IS_DK ? p.scale : 1.f;
-    if (p.mode == MODE_ROUNDS) {
-      float* dst = (IS_DK ? p.dk_acc : p.dv_acc) + ((int64_t)bh * p.SKV + mykey) * D;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d = 32 * dt + 8 * i + 4 * g;
-          f32x4 a = f32x4{acc[dt][4 * i] * sc, acc[dt][4 * i + 1] * sc, acc[dt][4 * i + 2] * sc,
-                          acc[dt][4 * i + 3] * sc};
-          if (acc_in) a += *(const f32x4*)(dst + d);
-          *(f32x4*)(dst + d) = a;
-        }
-    } else {
-      bf16* dst = IS_DK ? p.dk + b * p.sdk[0] + h * p.sdk[1] + mykey * p.sdk[2]
-                        : p.dv + b * p.sdv[0] + h * p.sdv[1] + mykey * p.sdv[2];
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d = 32 * dt + 8 * i + 4 * g;
-          *(u32x2*)(dst + d) = u32x2{pk_bf16(acc[dt][4 * i] * sc, acc[dt][4 * i + 1] * sc),
-                                     pk_bf16(acc[dt][4 * i + 2] * sc, acc[dt][4 * i + 3] * sc)};
-        }
+      xb[2 * u] = pack8(sacc[u], 0);
+      xb[2 * u + 1] = pack8(sacc[u], 1);
     }
   };
-  if (wave >= 4)
-    run(std::true_type{});
-  else
-    run(std::false_type{});
+
+  auto run = [&](auto ROLE_B) {
+    constexpr bool RB = decltype(ROLE_B)::value;
+    // ---- prologue: tile 0 in buffer 0, each group's next tile in flight
+    It tw = tv;  // next tile this thread's group stages
+    load_tile(tw);
+    store_tile(0);
+    advance(tw);
+    __syncthreads();
+    if constexpr (!RB) {
+      first_s(ROLE_B);  // slot 0
+    } else {
+      __syncthreads();  // slot 0: idle
+      first_s(ROLE_B);  // slot 1
+    }
+#pragma unroll
+    for (int u = 0; u < BQ / 32; ++u) {
+      hold(sacc[u]);
+      if constexpr (RB) hold(pacc[u]);
+    }
+    __syncthreads();
+    // settle the prologue's global loads here, not inside the loop
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      hold(kreg[s]);
+      if constexpr (RB) hold(vreg[s]);
+    }
+    int it = 0;
+    while (tv.r < nseg) {
+      const int cur = it % 3, nxt = (it + 1) % 3;
+      // Tile it+1 is loaded at the head of the VALU slot and written to LDS at
+      // its end, so the staging registers are free during the MFMA slot.
+      const bool stage = tw.r < nseg;
+      if (stage) load_tile(tw);
+      phase_valu(ROLE_B, tv);
+#pragma unroll
+      for (int t = 0; t < BQ / 16; ++t) hold(xb[t]);
+      if (stage) {
+        store_tile(nxt);
+        advance(tw);
+      }
+      __syncthreads();
+      It tn = tv;
+      advance(tn);
+      mfma_slot(ROLE_B, cur, nxt);  // after the last tile S (dP) read a stale buffer, unused
+#pragma unroll
+      for (int u = 0; u < BQ / 32; ++u) {
+        hold(sacc[u]);
+        if constexpr (RB) hold(pacc[u]);
+      }
+      // group A closes this slot; group B's last MFMA slot is the final one
+      if (!RB || tn.r < nseg) __syncthreads();
+      tv = tn;
+      ++it;
+    }
+  };
+  // (a job without query tiles skips all of it, so both groups meet the same barriers)
+  if (tv.r < nseg) {
+    if (groupB)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
+  }
+
+  if (!key_ok) return;
+  const float sc = groupB ? p.scale : 1.f;
+  if (p.mode == MODE_ROUNDS) {
+    float* dst = (groupB ? p.dk_acc : p.dv_acc) + ((int64_t)bh * p.SKV + mykey) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 32 * dt + 8 * i + 4 * g;
+        f32x4 a = f32x4{acc[dt][4 * i] * sc, acc[dt][4 * i + 1] * sc, acc[dt][4 * i + 2] * sc,
+                        acc[dt][4 * i + 3] * sc};
+        if (acc_in) a += *(const f32x4*)(dst + d);
+        *(f32x4*)(dst + d) = a;
+      }
+  } else {
+    bf16* dst = groupB ? p.dk + b * p.sdk[0] + h * p.sdk[1] + mykey * p.sdk[2]
+                       : p.dv + b * p.sdv[0] + h * p.sdv[1] + mykey * p.sdv[2];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 32 * dt + 8 * i + 4 * g;
+        *(u32x2*)(dst + d) = u32x2{pk_bf16(acc[dt][4 * i] * sc, acc[dt][4 * i + 1] * sc),
+                                   pk_bf16(acc[dt][4 * i + 2] * sc, acc[dt][4 * i + 3] * sc)};
+      }
+  }
 }
 
 // ---------------------------------------------------------------- dQ (Q-stationary)
@@ -358,25 +487,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
 // and group B the same one slot later, except that it writes V(t+2) in its
 // VALU slot 2t+2 (V(1) in slot 0), so a tile's V is visible one slot before
 // group A's S/dP of that tile.  Tiles rotate through three LDS buffers; each
-// half of a buffer is rewritten only after its last reader's slot.  Tile rows
-// are laid out in groups of four: rows of a group 320 bytes apart (64 mod 256)
-// and groups 1232 bytes apart (16 mod 64).  Sixteen consecutive rows then
-// start in sixteen distinct 16-byte bank slots (row reads of S and dP by
-// ds_read_b128, one row per lane), and four rows of a group cover all 64
-// banks with 64 bytes each (transposing reads of K^T by ds_read_b64_tr_b16),
-// while every address stays a lane base plus a constant.
-
-template <typename T>
-__device__ inline void hold(T& x) {  // materialise x here: an empty asm that reads and writes it
-  asm volatile("" : "+v"(x));
-}
-
-// Row r of a dQ-kernel tile starts at element rbase(r) (see above).
-constexpr int kRowStr = D + 32, kGrpStr = 3 * kRowStr + D + 8;
-__device__ inline int rbase(int r) { return (r >> 2) * kGrpStr + (r & 3) * kRowStr; }
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+// half of a buffer is rewritten only after its last reader's slot.
 
 __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdParams p) {
   constexpr int BM = 32 * kDqWaves, BN = 64, GT = 64 * kDqWaves / 2;
@@ -514,10 +625,8 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdParams p) {
       }
   };
   // dQ^T += K^T dS^T: the A operand of step t covers keys 16t+4g+{0..3} and
-  // 16t+4g+8+{0..3} of head dims 32dt + lane%32, the key order of dsb[t]; lane
-  // address: row 16t + 4g + li/4 (group 4t + g), column 32dt + 16*(lane/16 % 2) + 4*(li % 4)
-  const int li = lane & 15;
-  const int tb = g * kGrpStr + (li >> 2) * kRowStr + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
+  // 16t+4g+8+{0..3} of head dims 32dt + lane%32, the key order of dsb[t]
+  const int tb = trb(lane);
   // One MFMA slot as a fixed sequence: dQ of the current tile (16 MFMAs), then
   // S and dP of the next (32).  The A operand of MFMA m + DIST is read from
   // LDS just before MFMA m is issued and a scheduling barrier follows every
@@ -527,12 +636,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdParams p) {
   auto op_read = [&](auto M, int cur_buf, int nxt_buf) -> bf16x8 {
     constexpr int m = decltype(M)::value;
     if constexpr (m < NDQ) {
-      constexpr int t = m / (D / 32), dt = m % (D / 32);
-      const bf16* a0 = smem + cur_buf * STAGE + tb + 4 * t * kGrpStr + 32 * dt;
-      s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
-      s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0 + 2 * kGrpStr));
-      u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-      return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+      return tr_rows(smem + cur_buf * STAGE + tb, m / (D / 32), m % (D / 32));
     } else {
       constexpr int q = m - NDQ, s = q / 4, u = (q / 2) % 2, kind = q % 2;
       return *(const bf16x8*)(smem + nxt_buf * STAGE + kind * TILE + rb + u * 8 * kGrpStr + 16 * s);
