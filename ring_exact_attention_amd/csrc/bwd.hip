@@ -128,18 +128,20 @@ __device__ inline int trb(int lane) {
 // 128 keys per workgroup; 8 waves in two roles over the same four 32-key
 // groups: waves 0-3 (group A) accumulate dV, waves 4-7 (group B) dK, and wave
 // w shares its SIMD with wave w+4.  Splitting by output keeps each wave within
-// half the register file (A holds K and dV, B holds K, V and dK); the price is
-// that S is computed by both roles.  Queries stream in tiles of 64 rows, and
-// the two groups alternate like the dQ kernel's, one phase apart:
-//   A: MFMA  dV^T += dO^T P (tile j-1), S = Q K^T (tile j)            32 MFMAs
-//      VALU  P = exp2(S scale log2(e) - LSE log2(e)), writes Q(j+1), LSE, Delta
-//   B: MFMA  dK^T += Q^T dS (tile j-1), S and dP = dO V^T (tile j)    48 MFMAs
-//      VALU  dS = P o (dP - Delta), writes dO(j+1)
+// half the register file (A holds K and dV, B holds V and dK).  A computes
+// P and hands it, rounded to bf16, to B through LDS.  Queries stream in tiles
+// of 64 rows, and the two groups alternate like the dQ kernel's, one phase
+// apart:
+//   A: MFMA  dV^T += dO^T P (tile j-1), S = Q K^T (tile j)         32 MFMAs
+//      VALU  P = exp2(S scale log2(e) - LSE log2(e)) to LDS, writes Q(j+1), LSE
+//   B: MFMA  dK^T += Q^T dS (tile j-1), dP = dO V^T (tile j)       32 MFMAs
+//      VALU  dS = P o (dP - Delta) with P from LDS, writes dO(j+1), Delta
 // Slots from 0:  A: slot 0: S(0);  2j+1: P(j);  2j+2: dV(j), S(j+1)
-//                B: slot 1: S/dP(0);  2j+2: dS(j);  2j+3: dK(j), S/dP(j+1)
-// Q tiles (with their rows' LSE and Delta) and dO tiles rotate through three
-// LDS buffers; Q(j) is read from slot 2j to 2j+3 and rewritten (as Q(j+3)) in
-// slot 2j+5, dO(j) is read in slots 2j+1 and 2j+2 and rewritten in slot 2j+6.
+//                B: slot 1: dP(0);  2j+2: dS(j);  2j+3: dK(j), dP(j+1)
+// Q tiles (with their rows' LSE) and dO tiles (with Delta) rotate through
+// three LDS buffers; Q(j) is read from slot 2j to 2j+3 and rewritten (as
+// Q(j+3)) in slot 2j+5, dO(j) is read in slots 2j+1 and 2j+2 and rewritten in
+// slot 2j+6.  P(j) is written in slot 2j+1 and read in slot 2j+2.
 
 // dK/dV: 8 waves in two roles; dQ: 8 waves, two per SIMD.
 constexpr int kDkdvWaves = 8, kDqWaves = 8;
@@ -151,6 +153,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
   static_assert(KC * GT == BQ * D / 8, "staging must divide evenly");
   __shared__ __attribute__((aligned(16))) bf16 smem[NBUF * STAGE];
   __shared__ float s_lse[NBUF][BQ], s_dlt[NBUF][BQ];
+  __shared__ __attribute__((aligned(16))) bf16 s_p[4][BQ / 16][64 * 8];  // P per A wave, B-operand order
 
   int g_, t_;
   if (!xcd_group_tile(blockIdx.x, p.tiles, p.groups, &g_, &t_)) return;
@@ -187,17 +190,8 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
   const float* lseg = p.lse + (int64_t)bh * p.SQ;
   const float* dltg = p.delta + (int64_t)bh * p.SQ;
 
-  // K (both roles) and V (dK role) rows of this lane's key, as B operands
-  bf16x8 kreg[D / 16], vreg[D / 16];
-  {
-    const bf16* kp = p.k + b * p.sk[0] + h * p.sk[1] + mykey * p.sk[2];
-    const bf16* vp = p.v + b * p.sv[0] + h * p.sv[1] + mykey * p.sv[2];
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      kreg[s] = key_ok ? *(const bf16x8*)(kp + 16 * s + 8 * g) : bf16x8{};
-      vreg[s] = (key_ok && groupB) ? *(const bf16x8*)(vp + 16 * s + 8 * g) : bf16x8{};
-    }
-  }
+  // B operand rows of this lane's key: K (role A, for S) or V (role B, for dP)
+  bf16x8 breg[D / 16];
   f32x16 acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
@@ -256,11 +250,14 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
       const uint32_t off = __umul24((uint32_t)r, sstr2) + (uint32_t)(scol * 16);
       stg[i] = *(const u32x4*)(base + off);
     }
-    if (!groupB && gtid < BQ) {
+    if (gtid < BQ) {
       const int64_t row = t.qt + gtid;
-      const float l = gtid < lim ? lseg[row] : -INFINITY;
-      st_l = (l == -INFINITY) ? -INFINITY : -l * rscale;  // -inf: the row takes no weight
-      st_d = gtid < lim ? -dltg[row] : 0.f;
+      if (!groupB) {
+        const float l = gtid < lim ? lseg[row] : -INFINITY;
+        st_l = (l == -INFINITY) ? -INFINITY : -l * rscale;  // -inf: the row takes no weight
+      } else {
+        st_d = gtid < lim ? -dltg[row] : 0.f;
+      }
     }
   };
   const int wbase = soff + rbase(srow0) + scol * 8;
@@ -268,9 +265,11 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
     bf16* dst = smem + buf * STAGE + wbase;
 #pragma unroll
     for (int i = 0; i < KC; ++i) *(u32x4*)(dst + i * (srstep / 4) * kGrpStr) = stg[i];
-    if (!groupB && gtid < BQ) {
-      s_lse[buf][gtid] = st_l;
-      s_dlt[buf][gtid] = st_d;
+    if (gtid < BQ) {
+      if (!groupB)
+        s_lse[buf][gtid] = st_l;
+      else
+        s_dlt[buf][gtid] = st_d;
     }
   };
 
@@ -279,39 +278,36 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
   const int rb = rbase(lr) + 8 * g;  // this lane's row-read base
   const int tb = trb(lane);
   // One MFMA slot as a fixed sequence: dV or dK of the current tile (16
-  // MFMAs), then S (and dP) of the next (16 or 32).  The A operand of MFMA
+  // MFMAs), then S (A) or dP (B) of the next (16).  The A operand of MFMA
   // m + DIST is read from LDS just before MFMA m is issued and a scheduling
   // barrier follows every MFMA, so each read has DIST MFMAs to arrive.
-  constexpr int NACC = (BQ / 16) * (D / 32), DIST = 2, NOB = DIST + 1, SEED_AHEAD = 4;
-  // S and dP accumulators seeded from LDS; element 4i+jj of block u is query
-  // row 32u + 8i + 4g + jj of the tile
-  auto seed = [&](bool rb_role, int buf) {
+  constexpr int NACC = (BQ / 16) * (D / 32), NSP = (D / 16) * (BQ / 32), NM = NACC + NSP;
+  constexpr int DIST = 4, NOB = DIST + 1, SEED_AHEAD = 4;
+  // S (A) or dP (B) accumulators seeded from LDS; element 4i+jj of block u is
+  // query row 32u + 8i + 4g + jj of the tile
+  auto seed = [&](auto ROLE_B, int buf) {
+    constexpr bool RB = decltype(ROLE_B)::value;
+    f32x16* dst = RB ? pacc : sacc;
+    const float* src = RB ? s_dlt[buf] : s_lse[buf];
 #pragma unroll
     for (int u = 0; u < BQ / 32; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int qo = 32 * u + 8 * i + 4 * g;
-        const f32x4 l4 = *(const f32x4*)(&s_lse[buf][qo]);
+        const f32x4 x4 = *(const f32x4*)(src + 32 * u + 8 * i + 4 * g);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) sacc[u][4 * i + jj] = l4[jj];
-        if (rb_role) {
-          const f32x4 d4 = *(const f32x4*)(&s_dlt[buf][qo]);
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) pacc[u][4 * i + jj] = d4[jj];
-        }
+        for (int jj = 0; jj < 4; ++jj) dst[u][4 * i + jj] = x4[jj];
       }
   };
   auto mfma_slot = [&](auto ROLE_B, int cur_buf, int nxt_buf) {
     constexpr bool RB = decltype(ROLE_B)::value;
-    constexpr int NM = NACC + (RB ? 2 : 1) * (D / 16) * (BQ / 32);
     auto rd = [&](auto M) -> bf16x8 {
       constexpr int m = decltype(M)::value;
       if constexpr (m < NACC) {  // dV: dO^T from the dO half; dK: Q^T from the Q half
         return tr_rows(smem + cur_buf * STAGE + (RB ? 0 : TILE) + tb, m / (D / 32), m % (D / 32));
       } else {  // S: Q rows; dP: dO rows
-        constexpr int q = m - NACC, per = RB ? 2 : 1;
-        constexpr int s = q / (per * (BQ / 32)), u = (q / per) % (BQ / 32), kind = q % per;
-        return *(const bf16x8*)(smem + nxt_buf * STAGE + kind * TILE + rb + u * 8 * kGrpStr + 16 * s);
+        constexpr int q = m - NACC, s = q / (BQ / 32), u = q % (BQ / 32);
+        return *(const bf16x8*)(smem + nxt_buf * STAGE + (RB ? TILE : 0) + rb + u * 8 * kGrpStr +
+                                16 * s);
       }
     };
     auto mf = [&](auto M, const bf16x8& a) {
@@ -320,12 +316,11 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
         constexpr int t = m / (D / 32), dt = m % (D / 32);
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xb[t], acc[dt], 0, 0, 0);
       } else {
-        constexpr int q = m - NACC, per = RB ? 2 : 1;
-        constexpr int s = q / (per * (BQ / 32)), u = (q / per) % (BQ / 32), kind = q % per;
-        if constexpr (kind == 0)
-          sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[s], sacc[u], 0, 0, 0);
+        constexpr int q = m - NACC, s = q / (BQ / 32), u = q % (BQ / 32);
+        if constexpr (!RB)
+          sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, breg[s], sacc[u], 0, 0, 0);
         else
-          pacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vreg[s], pacc[u], 0, 0, 0);
+          pacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, breg[s], pacc[u], 0, 0, 0);
       }
     };
     bf16x8 ob[NOB];
@@ -333,56 +328,76 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
     static_for<0, NM>([&](auto M) {
       constexpr int m = decltype(M)::value;
       // seeds late in the dV/dK part, when most of xb is dead
-      if constexpr (m == NACC - SEED_AHEAD) seed(RB, nxt_buf);
+      if constexpr (m == NACC - SEED_AHEAD) seed(ROLE_B, nxt_buf);
       if constexpr (m + DIST < NM) ob[(m + DIST) % NOB] = rd(std::integral_constant<int, m + DIST>{});
       mf(M, ob[m % NOB]);
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  // S-only prologue slot (tile 0 in buffer 0)
+  // S (A) or dP (B) of tile 0, in buffer 0
   auto first_s = [&](auto ROLE_B) {
     constexpr bool RB = decltype(ROLE_B)::value;
-    seed(RB, 0);
-    const bf16* qs = smem + rb;
+    seed(ROLE_B, 0);
+    const bf16* src = smem + (RB ? TILE : 0) + rb;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
 #pragma unroll
       for (int u = 0; u < BQ / 32; ++u) {
-        const int off = u * 8 * kGrpStr + 16 * s;
-        sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qs + off), kreg[s],
-                                                          sacc[u], 0, 0, 0);
-        if constexpr (RB)
-          pacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qs + TILE + off),
-                                                            vreg[s], pacc[u], 0, 0, 0);
+        const bf16x8 a = *(const bf16x8*)(src + u * 8 * kGrpStr + 16 * s);
+        if constexpr (!RB)
+          sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, breg[s], sacc[u], 0, 0, 0);
+        else
+          pacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, breg[s], pacc[u], 0, 0, 0);
       }
   };
   const float c2 = p.scale_log2;
-  // P (A) or dS (B) of a tile; element 4i+jj of block u is query qt + 32u + 8i + 4g + jj
+  // A: P of a tile (element 4i+jj of block u is query qt + 32u + 8i + 4g + jj),
+  // kept in xb and copied to s_p for B.  B: dS = P o (dP - Delta) with P from s_p.
+  bf16* const pslot = &s_p[wave & 3][0][lane * 8];
   auto phase_valu = [&](auto ROLE_B, const It& t) {
     constexpr bool RB = decltype(ROLE_B)::value;
-    const bool need_mask = p.causal && t.qt < kw0 + 31;
-    // query offsets below lim precede this lane's key: no weight
-    const int lim = need_mask ? (int)max(min(mykey - t.qt, (int64_t)BQ), (int64_t)0) : 0;
+    if constexpr (!RB) {
+      const bool need_mask = p.causal && t.qt < kw0 + 31;
+      // query offsets below lim precede this lane's key: no weight
+      const int lim = need_mask ? (int)max(min(mykey - t.qt, (int64_t)BQ), (int64_t)0) : 0;
 #pragma unroll
-    for (int u = 0; u < BQ / 32; ++u) {  // one 32-query block at a time
+      for (int u = 0; u < BQ / 32; ++u) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[u][e] = __builtin_amdgcn_exp2f(sacc[u][e] * c2);  // P
-      if (need_mask) {
+        for (int e = 0; e < 16; ++e) sacc[u][e] = __builtin_amdgcn_exp2f(sacc[u][e] * c2);
+        if (need_mask) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (32 * u + 8 * (e / 4) + 4 * g + (e % 4) < lim) sacc[u][e] = 0.f;
+          for (int e = 0; e < 16; ++e)
+            if (32 * u + 8 * (e / 4) + 4 * g + (e % 4) < lim) sacc[u][e] = 0.f;
+        }
+        xb[2 * u] = pack8(sacc[u], 0);
+        xb[2 * u + 1] = pack8(sacc[u], 1);
       }
-      if constexpr (RB) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[u][e] *= pacc[u][e];  // dS (unscaled)
+      for (int q = 0; q < BQ / 16; ++q) *(bf16x8*)(pslot + q * 64 * 8) = xb[q];
+    } else {
+#pragma unroll
+      for (int u = 0; u < BQ / 32; ++u) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const bf16x8 pv = *(const bf16x8*)(pslot + (2 * u + hh) * 64 * 8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pacc[u][8 * hh + e] *= (float)pv[e];  // dS (unscaled)
+        }
+        xb[2 * u] = pack8(pacc[u], 0);
+        xb[2 * u + 1] = pack8(pacc[u], 1);
       }
-      xb[2 * u] = pack8(sacc[u], 0);
-      xb[2 * u + 1] = pack8(sacc[u], 1);
     }
   };
 
   auto run = [&](auto ROLE_B) {
     constexpr bool RB = decltype(ROLE_B)::value;
+    {
+      const bf16* src = RB ? p.v + b * p.sv[0] + h * p.sv[1] + mykey * p.sv[2]
+                           : p.k + b * p.sk[0] + h * p.sk[1] + mykey * p.sk[2];
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+        breg[s] = key_ok ? *(const bf16x8*)(src + 16 * s + 8 * g) : bf16x8{};
+    }
     // ---- prologue: tile 0 in buffer 0, each group's next tile in flight
     It tw = tv;  // next tile this thread's group stages
     load_tile(tw);
@@ -397,16 +412,13 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
     }
 #pragma unroll
     for (int u = 0; u < BQ / 32; ++u) {
-      hold(sacc[u]);
+      if constexpr (!RB) hold(sacc[u]);
       if constexpr (RB) hold(pacc[u]);
     }
     __syncthreads();
     // settle the prologue's global loads here, not inside the loop
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      hold(kreg[s]);
-      if constexpr (RB) hold(vreg[s]);
-    }
+    for (int s = 0; s < D / 16; ++s) hold(breg[s]);
     int it = 0;
     while (tv.r < nseg) {
       const int cur = it % 3, nxt = (it + 1) % 3;
@@ -427,7 +439,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
       mfma_slot(ROLE_B, cur, nxt);  // after the last tile S (dP) read a stale buffer, unused
 #pragma unroll
       for (int u = 0; u < BQ / 32; ++u) {
-        hold(sacc[u]);
+        if constexpr (!RB) hold(sacc[u]);
         if constexpr (RB) hold(pacc[u]);
       }
       // group A closes this slot; group B's last MFMA slot is the final one
