@@ -215,7 +215,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only (the n ring workers are n KV shards "
+        print("bench.py: measures one GPU only (the n ring workers are n KV shards "
               "on one device); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
