@@ -250,14 +250,12 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
       const uint32_t off = __umul24((uint32_t)r, sstr2) + (uint32_t)(scol * 16);
       stg[i] = *(const u32x4*)(base + off);
     }
-    if (gtid < BQ) {
+    if (gtid < BQ) {  // raw values; transformed when written, after the VALU work
       const int64_t row = t.qt + gtid;
-      if (!groupB) {
-        const float l = gtid < lim ? lseg[row] : -INFINITY;
-        st_l = (l == -INFINITY) ? -INFINITY : -l * rscale;  // -inf: the row takes no weight
-      } else {
-        st_d = gtid < lim ? -dltg[row] : 0.f;
-      }
+      if (!groupB)
+        st_l = gtid < lim ? lseg[row] : -INFINITY;
+      else
+        st_d = gtid < lim ? dltg[row] : 0.f;
     }
   };
   const int wbase = soff + rbase(srow0) + scol * 8;
@@ -267,9 +265,9 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
     for (int i = 0; i < KC; ++i) *(u32x4*)(dst + i * (srstep / 4) * kGrpStr) = stg[i];
     if (gtid < BQ) {
       if (!groupB)
-        s_lse[buf][gtid] = st_l;
+        s_lse[buf][gtid] = (st_l == -INFINITY) ? -INFINITY : -st_l * rscale;  // -inf: no weight
       else
-        s_dlt[buf][gtid] = st_d;
+        s_dlt[buf][gtid] = -st_d;
     }
   };
 
