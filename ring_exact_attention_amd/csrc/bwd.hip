@@ -146,6 +146,8 @@ __device__ inline int trb(int lane) {
 // dK/dV: 8 waves in two roles; dQ: 8 waves, two per SIMD.
 constexpr int kDkdvWaves = 8, kDqWaves = 8;
 
+// CAUSAL instantiates the masking code; p.causal must agree.
+template <bool CAUSAL>
 __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int BK = 128, BQ = 64, GT = 64 * kDkdvWaves / 2;
   constexpr int TILE = BQ / 4 * kGrpStr, STAGE = 2 * TILE, NBUF = 3;
@@ -355,7 +357,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
   auto phase_valu = [&](auto ROLE_B, const It& t) {
     constexpr bool RB = decltype(ROLE_B)::value;
     if constexpr (!RB) {
-      const bool need_mask = p.causal && t.qt < kw0 + 31;
+      const bool need_mask = CAUSAL && t.qt < kw0 + 31;
       // query offsets below lim precede this lane's key: no weight
       const int lim = need_mask ? (int)max(min(mykey - t.qt, (int64_t)BQ), (int64_t)0) : 0;
 #pragma unroll
@@ -884,7 +886,12 @@ hipError_t bwd_run(const BwdArgs& a, hipStream_t st) {
     p.round = r;
     p.groups = groups;
     p.tiles = kv_tiles;
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(xcd_grid_size(kv_tiles, groups)), dim3(64 * kDkdvWaves), 0, st, p);
+    if (p.causal)
+      hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3(xcd_grid_size(kv_tiles, groups)),
+                         dim3(64 * kDkdvWaves), 0, st, p);
+    else
+      hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3(xcd_grid_size(kv_tiles, groups)),
+                         dim3(64 * kDkdvWaves), 0, st, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     p.tiles = q_tiles;
     hipLaunchKernelGGL(bwd_dq_kernel, dim3(xcd_grid_size(q_tiles, groups)), dim3(64 * kDqWaves), 0, st, p);
