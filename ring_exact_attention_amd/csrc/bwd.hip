@@ -501,6 +501,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
 // group A's S/dP of that tile.  Tiles rotate through three LDS buffers; each
 // half of a buffer is rewritten only after its last reader's slot.
 
+template <bool CAUSAL>
 __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdParams p) {
   constexpr int BM = 32 * kDqWaves, BN = 64, GT = 64 * kDqWaves / 2;
   constexpr int TILE = BN / 4 * kGrpStr, STAGE = 2 * TILE, NBUF = 3;
@@ -594,18 +595,23 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdParams p) {
   const int srow0 = gtid / (D / 8), scol = gtid % (D / 8);
   constexpr int srstep = GT / (D / 8);
   u32x4 stg[KC];
-  // Rows at or past the segment end repeat its last key (masked below).  Row
-  // strides are below 16 MiB (checked on the host), so a chunk's byte offset
-  // from the tile's first row is a 24-bit product.
+  // Rows at or past the segment end: V rows repeat its last key, K rows are
+  // written as zeros, so those keys add nothing to dQ = dS K whatever their dS
+  // and need no mask in the VALU slot.  Row strides are below 16 MiB (checked
+  // on the host), so a chunk's byte offset from the tile's first row is a
+  // 24-bit product.
   const uint32_t sstr2 = (uint32_t)(sstr * 2);
+  uint32_t szero = 0;  // chunks of the loaded tile to write as zeros (bit i: chunk i)
   auto load_tile = [&](const It& t) {
     const int lim = (int)min(t.ke - t.kt, (int64_t)BN);
     const char* base = (const char*)(ssrc + t.kt * sstr);
+    szero = 0;
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
       const int r = min(srow0 + i * srstep, lim - 1);
       const uint32_t off = __umul24((uint32_t)r, sstr2) + (uint32_t)(scol * 16);
       stg[i] = *(const u32x4*)(base + off);
+      if (!groupB && srow0 + i * srstep >= lim) szero |= 1u << i;
     }
   };
   static_assert(srstep % 4 == 0, "staging rows keep their place in a row group");
@@ -613,7 +619,8 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdParams p) {
   auto store_tile = [&](int buf) {
     bf16* dst = smem + buf * STAGE + wbase;
 #pragma unroll
-    for (int i = 0; i < KC; ++i) *(u32x4*)(dst + i * (srstep / 4) * kGrpStr) = stg[i];
+    for (int i = 0; i < KC; ++i)
+      *(u32x4*)(dst + i * (srstep / 4) * kGrpStr) = ((szero >> i) & 1) ? u32x4{} : stg[i];
   };
 
   f32x16 sacc[BN / 32], pacc[BN / 32];
@@ -682,13 +689,10 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdParams p) {
   };
   const float c2 = p.scale_log2;
   auto phase_ds = [&](const It& t) {
-    const bool need_mask = (t.kt + BN > t.ke) || (p.causal && t.kt + BN - 1 > wrow0);
-    int lim = BN;  // this row sees keys kt .. kt+lim-1 of the tile
-    if (need_mask) {
-      int64_t l = min(t.ke - t.kt, (int64_t)BN);
-      if (p.causal && myrow + 1 - t.kt < l) l = myrow + 1 - t.kt;
-      lim = (int)max(l, (int64_t)0);
-    }
+    // causal: this row sees keys kt .. kt+lim-1 of the tile (keys past the
+    // segment end have zero K rows, see load_tile)
+    const bool need_mask = CAUSAL && t.kt + BN - 1 > wrow0;
+    const int lim = need_mask ? (int)max(min(myrow + 1 - t.kt, (int64_t)BN), (int64_t)0) : BN;
 #pragma unroll
     for (int u = 0; u < BN / 32; ++u)
 #pragma unroll
@@ -894,7 +898,12 @@ hipError_t bwd_run(const BwdArgs& a, hipStream_t st) {
                          dim3(64 * kDkdvWaves), 0, st, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     p.tiles = q_tiles;
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3(xcd_grid_size(q_tiles, groups)), dim3(64 * kDqWaves), 0, st, p);
+    if (p.causal)
+      hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3(xcd_grid_size(q_tiles, groups)),
+                         dim3(64 * kDqWaves), 0, st, p);
+    else
+      hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3(xcd_grid_size(q_tiles, groups)),
+                         dim3(64 * kDqWaves), 0, st, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (p.mode == MODE_ROUNDS) {
