@@ -18,9 +18,9 @@
 // LDS with rows padded by 16 bytes (conflict-free 16-byte operand reads).
 // Within a stage the 32 MFMAs of a wave are issued in a fixed order, the
 // operands of each 16-element k-step read during the previous one; the
-// chunks staged for the next stage go to the other buffer one per MFMA at
-// the head of the stage, and the global loads of the stage after that are
-// issued one per MFMA at its tail (so their data has a whole stage to land).
+// chunks staged for the next stage go to the other buffer one every four
+// MFMAs, each followed two MFMAs later by the load (into the same registers)
+// of that chunk for the stage after it, which then has a whole stage to land.
 // Bursts of wide LDS writes fill the LDS data FIFO and stall every wave's
 // LDS reads; spreading them and the reads over the MFMAs is worth 14% here.
 // Workgroups that share a y tile are placed consecutively on one XCD so the
@@ -135,6 +135,7 @@ __global__ __launch_bounds__(T::NT) void gemm_kv_kernel(GemmParams p) {
   // the next stage written into buf^1 one per MFMA, then (LD) the loads of
   // the stage after it issued one per MFMA, so neither the LDS writes nor
   // the global loads arrive in bursts.
+  static_assert(NM % KC == 0, "staging chunks spread evenly over a stage's MFMAs");
   auto stage = [&](auto wr_, auto ld_, int buf, int e_next) __attribute__((always_inline)) {
     constexpr bool WR = decltype(wr_)::value, LD = decltype(ld_)::value;
     bf16x8 op[2][NOP];
@@ -148,8 +149,8 @@ __global__ __launch_bounds__(T::NT) void gemm_kv_kernel(GemmParams p) {
       acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[ks & 1][a], op[ks & 1][T::FA + b],
                                                           acc[a][b], 0, 0, 0);
       if constexpr (ks + 1 < KSN && idx < NOP) op[(ks + 1) & 1][idx] = rd(buf, ks + 1, idx);
-      if constexpr (WR && m < KC) store1(m, buf ^ 1);
-      if constexpr (LD && m >= NM - KC) load1(m - (NM - KC), e_next);
+      if constexpr (WR && m % (NM / KC) == 0) store1(m / (NM / KC), buf ^ 1);
+      if constexpr (LD && m % (NM / KC) == (NM / KC) / 2) load1(m / (NM / KC), e_next);
     });
     __builtin_amdgcn_sched_barrier(0);
   };

@@ -69,16 +69,18 @@ __device__ inline bf16x8 read_op(const bf16* As, const bf16* Bs, int ks, int o, 
 }
 
 // One stage of MFMAs from (As, Bs) in a fixed issue order, each k-step's
-// operands read during the previous one.  Chunk hooks run beside the MFMAs:
-// write(i) for i < NCH at the head (the next stage's staged chunks into the
-// other buffer) and load(i) at the tail (the loads of the stage after it),
-// so neither LDS writes nor global loads come in bursts.
+// operands read during the previous one.  Chunk hooks run beside the MFMAs,
+// one of each every NM/NCH MFMAs: write(i) (the next stage's staged chunk i
+// into the other buffer), then load(i) (chunk i of the stage after it, into
+// the registers just written out), so neither LDS writes nor global loads
+// come in bursts and every load has a whole stage to land.
 constexpr int NCH = 8;  // 16-byte staging chunks per thread and stage
 template <bool AT, bool WR, bool LD, typename W, typename L>
 __device__ inline __attribute__((always_inline)) void mma_stage(
     const bf16* As, const bf16* Bs, int wm, int wn, int lane, f32x16 (&acc)[FA][FB], W&& write,
     L&& load) {
   constexpr int NOP = FA + FB, KSN = TK / 16, NM = KSN * FA * FB;
+  static_assert(NM % NCH == 0, "staging chunks spread evenly over a stage's MFMAs");
   bf16x8 op[2][NOP];
 #pragma unroll
   for (int o = 0; o < NOP; ++o) op[0][o] = read_op<AT>(As, Bs, 0, o, wm, wn, lane);
@@ -91,8 +93,8 @@ __device__ inline __attribute__((always_inline)) void mma_stage(
                                                         acc[a][b], 0, 0, 0);
     if constexpr (ks + 1 < KSN && idx < NOP)
       op[(ks + 1) & 1][idx] = read_op<AT>(As, Bs, ks + 1, idx, wm, wn, lane);
-    if constexpr (WR && m < NCH) write(m);
-    if constexpr (LD && m >= NM - NCH) load(m - (NM - NCH));
+    if constexpr (WR && m % (NM / NCH) == 0) write(m / (NM / NCH));
+    if constexpr (LD && m % (NM / NCH) == (NM / NCH) / 2) load(m / (NM / NCH));
   });
   __builtin_amdgcn_sched_barrier(0);
 }
