@@ -224,8 +224,9 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
   seek(tv, 0);
   if (tv.r >= nseg && acc_in) return;  // nothing to add this round
 
-  // staging: group A moves Q tiles (and the rows' LSE, Delta), group B dO
-  // tiles; thread chunks are rows srow0 + 16 i of a tile at chunk column scol
+  // staging: group A moves Q tiles and their rows' LSE, group B dO tiles and
+  // their rows' Delta; thread chunks are rows srow0 + 16 i of a tile at chunk
+  // column scol
   const bf16* ssrc = groupB ? dog : qg;
   const int64_t sstr = groupB ? p.sdo[2] : p.sq[2];
   const int soff = groupB ? TILE : 0;
@@ -239,9 +240,9 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
   // reads in the VALU phase.
   float st_l = 0.f, st_d = 0.f;
   const float rscale = 1.f / p.scale;
-  // Rows at or past the segment end repeat its last row and get LSE = +inf
-  // (no weight).  Row strides are below 16 MiB (checked on the host), so a
-  // chunk's byte offset from the tile's first row is a 24-bit product.
+  // Rows at or past the segment end repeat its last row and get the S seed
+  // -inf (no weight).  Row strides are below 16 MiB (checked on the host), so
+  // a chunk's byte offset from the tile's first row is a 24-bit product.
   const uint32_t sstr2 = (uint32_t)(sstr * 2);
   auto load_tile = [&](const It& t) {
     const int lim = (int)min(t.qe - t.qt, (int64_t)BQ);
