@@ -151,11 +151,20 @@ def _causal(c) -> int:
     return int(bool(c))
 
 
+def _need_f32(name, t, numel):
+    """t must be a contiguous float32 device tensor of exactly `numel` elements:
+    the library indexes such buffers by row and cannot size-check them."""
+    if t.dtype != torch.float32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous float32")
+    if t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, {numel} expected")
+
+
 def bwa_partial_fwd(q, k, v, q0, nq, k0, nk, scale, causal, o_acc, lse_acc, accumulate):
     """One block pair merged into (o_acc fp32 [B,H,SQ,D], lse_acc fp32 [B,H,SQ])."""
-    for name, t in (("o_acc", o_acc), ("lse_acc", lse_acc)):
-        if t.dtype != torch.float32 or not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous float32")
+    B, H, SQ, D = q.shape
+    _need_f32("o_acc", o_acc, B * H * SQ * D)
+    _need_f32("lse_acc", lse_acc, B * H * SQ)
     tq, tk, tv = as_bwa(q), as_bwa(k), as_bwa(v)
     _check(lib().bwa_partial_fwd(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), q0, nq, k0,
                                  nk, float(scale), _causal(causal), _ptr(o_acc), _ptr(lse_acc),
@@ -173,6 +182,8 @@ def bwa_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None):
     rows = lse_a.numel()
     if o_a.numel() != rows * D or o_b.shape != o_a.shape or lse_b.shape != lse_a.shape:
         raise ValueError("merge operand shapes differ")
+    _need_f32("o_out", o_out, rows * D)
+    _need_f32("lse_out", lse_out, rows)
     _check(lib().bwa_merge(rows, D, _ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o_out),
                            _ptr(lse_out), _stream(o_a.device)))
     return o_out, lse_out
@@ -181,14 +192,20 @@ def bwa_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None):
 def bwa_merge_partials(o_parts, lse_parts, n, sched="kv", o=None, lse=None, dtype=None):
     """Merge n per-shard partials (o_parts fp32 [n,B,H,S_Q,D], lse_parts fp32
     [n,B,H,S_Q]) in each query block's ring order; returns (o, lse)."""
-    for t in (o_parts, lse_parts):
-        if t.dtype != torch.float32 or not t.is_contiguous():
-            raise ValueError("partials must be contiguous float32")
-    _, B, H, SQ, D = o_parts.shape
+    if o_parts.dim() != 5:
+        raise ValueError("o_parts must be [n, B, H, S_Q, D]")
+    m, B, H, SQ, D = o_parts.shape
+    if m != int(n):
+        raise ValueError(f"o_parts holds {m} partials, n = {n}")
+    _need_f32("o_parts", o_parts, m * B * H * SQ * D)
+    _need_f32("lse_parts", lse_parts, m * B * H * SQ)
     if o is None:
         o = torch.empty(B, H, SQ, D, dtype=dtype or torch.float32, device=o_parts.device)
     if lse is None:
         lse = torch.empty(B, H, SQ, dtype=torch.float32, device=o_parts.device)
+    if tuple(o.shape) != (B, H, SQ, D):
+        raise ValueError("o must be [B, H, S_Q, D] like the partials")
+    _need_f32("lse", lse, B * H * SQ)
     to = as_bwa(o)
     _check(lib().bwa_merge_partials(int(n), _sched(sched), _ptr(o_parts), _ptr(lse_parts),
                                     ctypes.byref(to), _ptr(lse), _stream(o_parts.device)))
@@ -233,8 +250,7 @@ def bwa_ring_fwd(q, k, v, n, sched="kv", mode="fused", causal=False, scale=None,
     scale = D ** -0.5 if scale is None else scale
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty(B, H, SQ, dtype=torch.float32, device=q.device) if lse is None else lse
-    if lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32")
+    _need_f32("lse", lse, B * H * SQ)
     m = _mode(mode)
     ws = _workspace(ring_fwd_workspace(q, k, n, m), q.device, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
@@ -258,8 +274,7 @@ def bwa_ring_bwd(q, k, v, o, lse, dout, n, sched="kv", mode="fused", causal=Fals
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    if lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32")
+    _need_f32("lse", lse, q.shape[0] * q.shape[1] * q.shape[2])
     m = _mode(mode)
     ws = _workspace(ring_bwd_workspace(q, k, n, m), q.device, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()

@@ -307,54 +307,56 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     lsum += (ts[0] + ts[1]) + (ts[2] + ts[3]);
   };
 
-  // ---- prologue: tile 0 into buffer 0, tile 1 in flight
+  // ---- prologue: tile 0 into buffer 0, tile 1 in flight.  A job without
+  // visible tiles skips the prologue and the loop altogether (the condition is
+  // uniform over the workgroup), so both groups always pass the same barriers.
   TileIter tw = tv;  // next tile this thread's group stages
   if (tv.valid(jb)) {
     load_tile(tw);
     store_tile(0);
     tw.advance(p, jb, BN);
     if (tw.valid(jb)) load_tile(tw);
-  }
-  __syncthreads();
-  if (!groupB) {
-    if (tv.valid(jb)) phase_s(0);  // slot 0
     __syncthreads();
-  } else {
-    __syncthreads();               // slot 0: idle
-    if (tv.valid(jb)) phase_s(0);  // slot 1
-    __syncthreads();
-  }
-  // Settle the prologue's global loads (Q, the carried accumulator) here: the
-  // wait-count pass cannot tell that the loop's first MFMAs already waited for
-  // them, and would otherwise wait on every tile's staging loads as well.
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) pin(qreg[s]);
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) pin(oacc[dt]);
-  int j = 0;
-  while (tv.valid(jb)) {
-    const int cur = j % 3, nxt = (j + 1) % 3;
-    phase_softmax(tv);
-#pragma unroll
-    for (int t = 0; t < BN / 16; ++t) pin(pb[t]);
-    pin(lsum);
-    if (tw.valid(jb)) {  // stage tile j+1, fetch tile j+2
-      store_tile(nxt);
-      tw.advance(p, jb, BN);
-      if (tw.valid(jb)) load_tile(tw);
+    if (!groupB) {
+      phase_s(0);  // slot 0
+      __syncthreads();
+    } else {
+      __syncthreads();  // slot 0: idle
+      phase_s(0);       // slot 1
+      __syncthreads();
     }
-    __syncthreads();
-    TileIter tn = tv;
-    tn.advance(p, jb, BN);
-    phase_pv(cur);
-    if (tn.valid(jb)) phase_s(nxt);
+    // Settle the prologue's global loads (Q, the carried accumulator) here: the
+    // wait-count pass cannot tell that the loop's first MFMAs already waited for
+    // them, and would otherwise wait on every tile's staging loads as well.
 #pragma unroll
-    for (int u = 0; u < BN / 32; ++u) pin(sacc[u]);
-    // group A closes this slot; group B's last MFMA slot is the final one
-    if (!groupB || tn.valid(jb)) __syncthreads();
-    tv = tn;
-    ++j;
-  }
+    for (int s = 0; s < D / 16; ++s) pin(qreg[s]);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) pin(oacc[dt]);
+    int j = 0;
+    while (tv.valid(jb)) {
+      const int cur = j % 3, nxt = (j + 1) % 3;
+      phase_softmax(tv);
+#pragma unroll
+      for (int t = 0; t < BN / 16; ++t) pin(pb[t]);
+      pin(lsum);
+      if (tw.valid(jb)) {  // stage tile j+1, fetch tile j+2
+        store_tile(nxt);
+        tw.advance(p, jb, BN);
+        if (tw.valid(jb)) load_tile(tw);
+      }
+      __syncthreads();
+      TileIter tn = tv;
+      tn.advance(p, jb, BN);
+      phase_pv(cur);
+      if (tn.valid(jb)) phase_s(nxt);
+#pragma unroll
+      for (int u = 0; u < BN / 32; ++u) pin(sacc[u]);
+      // group A closes this slot; group B's last MFMA slot is the final one
+      if (!groupB || tn.valid(jb)) __syncthreads();
+      tv = tn;
+      ++j;
+    }
+  }  // tv.valid(jb)
 
   // ---- epilogue
   const float ltot = wave_swap32_sum(lsum);

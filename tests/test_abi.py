@@ -242,3 +242,34 @@ def test_kv_recompute_bwd_validation(L):
            "share one layout")
     expect(L, call(outs=(None, None, None)), E.BWA_ERR_INVALID_ARG, "no output")
     expect(L, call(dk=T(S=64)), E.BWA_ERR_INVALID_ARG, "does not match")
+
+
+def test_binding_rejects_missized_buffers():
+    """Buffers the C ABI indexes by row without a size of their own (LSE,
+    accumulators, partials, merge outputs) are checked in the binding before
+    any pointer reaches the library (host only: the checks raise first)."""
+    import torch
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 16, 64, dtype=torch.bfloat16)
+    f = lambda *s: torch.zeros(*s, dtype=torch.float32)
+    with pytest.raises(ValueError, match="lse has"):
+        _bwa.bwa_ring_fwd(q, k, k, 2, lse=f(1, 2, 7))
+    with pytest.raises(ValueError, match="lse must be contiguous float32"):
+        _bwa.bwa_ring_fwd(q, k, k, 2, lse=f(1, 2, 16)[:, :, ::2])
+    with pytest.raises(ValueError, match="lse has"):
+        _bwa.bwa_ring_bwd(q, k, k, q, f(1, 2, 9), q, 2)
+    with pytest.raises(ValueError, match="o_acc has"):
+        _bwa.bwa_partial_fwd(q, k, k, 0, 8, 0, 16, 0.1, False, f(1, 2, 7, 64), f(1, 2, 8), False)
+    with pytest.raises(ValueError, match="lse_acc has"):
+        _bwa.bwa_partial_fwd(q, k, k, 0, 8, 0, 16, 0.1, False, f(1, 2, 8, 64), f(1, 2, 9), False)
+    with pytest.raises(ValueError, match="holds 3 partials"):
+        _bwa.bwa_merge_partials(f(3, 1, 2, 8, 64), f(3, 1, 2, 8), 4)
+    with pytest.raises(ValueError, match="lse_parts has"):
+        _bwa.bwa_merge_partials(f(3, 1, 2, 8, 64), f(3, 1, 2, 7), 3)
+    a, la = f(16, 64), f(16)
+    with pytest.raises(ValueError, match="o_out has"):
+        _bwa.bwa_merge(a, la, a, la, o_out=f(15, 64), lse_out=f(16))
+    with pytest.raises(ValueError, match="o_out must be contiguous float32"):
+        _bwa.bwa_merge(a, la, a, la, o_out=a.bfloat16(), lse_out=f(16))
+    with pytest.raises(ValueError, match="lse_out has"):
+        _bwa.bwa_merge(a, la, a, la, o_out=f(16, 64), lse_out=f(17))

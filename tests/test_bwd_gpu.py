@@ -118,9 +118,15 @@ def test_full_recompute_bwd(bwa, orc):
     do = make_dout(w, device="cuda")
     k, v = bwa.bwa_kv_recompute(y, wk, wv, w.H, w.D)
     o, lse = bwa.bwa_ring_fwd(q, k, v, w.n, "kv", "fused", scale=w.scale)
-    dq, dk, dv = bwa.bwa_ring_bwd(q, k, v, o, lse, do, w.n, "kv", "fused", scale=w.scale)
-    torch.cuda.synchronize()
-    for x in (k, v, o, dq, dk, dv):
+    grads = {}
+    for sched, mode in (("kv", "fused"), ("q", "fused"), ("kv", "rounds"), ("q", "rounds")):
+        log_case(workload=w.name, stage="backward", sched=sched, mode=mode)
+        dq, dk, dv = bwa.bwa_ring_bwd(q, k, v, o, lse, do, w.n, sched, mode, scale=w.scale)
+        torch.cuda.synchronize()
+        for x in (dq, dk, dv):
+            assert torch.isfinite(x).all()
+        grads[(sched, mode)] = (dq, dk, dv)
+    for x in (k, v, o):
         assert torch.isfinite(x).all()
 
     yc, wkc, wvc = y.cpu(), wk.cpu(), wv.cpu()
@@ -142,9 +148,11 @@ def test_full_recompute_bwd(bwa, orc):
     log_case(workload=w.name, stage="oracle backward")
     ref = orc.attn_bwd(qh, K, V, doh, w.scale, keys=keys)
     kk = torch.as_tensor(keys, device="cuda")
-    check_grad(dq[0, heads], ref["dq"], "dq full")
-    check_grad(dk[0, heads][:, kk], ref["dk"], "dk full (sampled keys)")
-    check_grad(dv[0, heads][:, kk], ref["dv"], "dv full (sampled keys)")
+    for (sched, mode), (dq, dk, dv) in grads.items():
+        tag = f"{sched}/{mode}"
+        check_grad(dq[0, heads], ref["dq"], f"dq full {tag}")
+        check_grad(dk[0, heads][:, kk], ref["dk"], f"dk full {tag} (sampled keys)")
+        check_grad(dv[0, heads][:, kk], ref["dv"], f"dv full {tag} (sampled keys)")
 
 
 # ---------------------------------------------------------------- gradients through the recompute
