@@ -39,8 +39,9 @@
  *       0: none;
  *       1: rows are in sequence order, key j visible to query i iff j <= i;
  *       2: rows are in the striped order over the n shards (bwa_ring_fwd
- *          only, n must divide S): shard w = rows [w*S/n, (w+1)*S/n) holds
- *          sequence positions w, w+n, w+2n, ... in order, and key j is
+ *          and bwa_ring_bwd, n must divide S): shard w = rows
+ *          [w*S/n, (w+1)*S/n) holds sequence positions w, w+n, w+2n, ... in
+ *          order, and key j is
  *          visible to query i iff its position is not after i's.  Every block
  *          pair is then about half visible, which balances a causal ring
  *          (Striped Attention's token assignment, named in the LV-XAttn
@@ -203,7 +204,11 @@ size_t bwa_ring_bwd_workspace(const bwa_tensor* q, const bwa_tensor* k, int n, b
  * treated as FUSED).
  *   o, dout [B, H, S_Q, D] and lse fp32 [B, H, S_Q] from the forward.
  *   dq [B, H, S_Q, D], dk and dv [B, H, S_KV, D] in q's dtype (overwritten).
- * Only bf16 with D = 128 is implemented (else BWA_ERR_UNSUPPORTED).
+ *   causal: 0, 1 or 2 as in the conventions above (the forward's value).
+ * bf16 only, D = 64 or 128 (fp32 inputs give BWA_ERR_UNSUPPORTED).
+ * workspace: at least bwa_ring_bwd_workspace() bytes, 256-byte aligned:
+ * Delta fp32 [B, H, S_Q] (every mode) and, for ROUNDS, fp32 dQ, dK, dV
+ * accumulators carried between the round launches.
  */
 bwa_status bwa_ring_bwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v,
                         const bwa_tensor* o, const float* lse, const bwa_tensor* dout, int n,
@@ -220,6 +225,10 @@ bwa_status bwa_ring_bwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tens
  *   y     bf16 [B, S_KV, E] contiguous.
  *   wk_t, wv_t bf16 [H*D, E] contiguous: W_k, W_v transposed (row n holds
  *         column n of W), the [out, in] layout of a linear layer's weight.
+ *         A caller holding W row-major as [E, H*D] passes its transpose
+ *         (one copy per weight update): both GEMM operands then have the
+ *         contraction index E contiguous, which the 16-byte operand loads
+ *         need.
  *   k, v  bf16 [B, H, S_KV, D] tensors (any strides per the conventions).
  * bf16 only; E must be a multiple of 64 and H*D a multiple of 128.
  */

@@ -223,8 +223,9 @@ def ring_fwd(q, k, v, scale: float, n: int, sched: int, causal: bool = False):
     return o, lse
 
 
-def attn_bwd(q, k, v, do, scale: float, causal: bool = False, heads=None, keys=None):
+def attn_bwd(q, k, v, do, scale: float, causal=False, heads=None, keys=None):
     """Exact gradient of softmax(tau Q K^T) V for the listed heads (flat b*H+h).
+    causal as in attn_fwd (False, True or ("striped", n)).
 
     Returns dict of float64 arrays: dq [nh,SQ,D], dk/dv [nh,nkeys,D],
     lse/delta [nh,SQ].  heads=None means every head; keys=None every key.
@@ -247,7 +248,8 @@ def attn_bwd(q, k, v, do, scale: float, causal: bool = False, heads=None, keys=N
     out = dict(dq=np.zeros((nh, SQ, D)), dk=np.zeros((nh, nk, D)), dv=np.zeros((nh, nk, D)),
                lse=np.zeros((nh, SQ)), delta=np.zeros((nh, SQ)))
     _load().orc_attn_bwd_heads(pq, pk, pv, pd, dt, ddo, B, H, SQ, SKV, D, float(scale),
-                               int(causal), hs.ctypes.data, nh, pks, nk if keys is not None else 0,
+                               _causal_code(causal), hs.ctypes.data, nh, pks,
+                               nk if keys is not None else 0,
                                out["dq"].ctypes.data, out["dk"].ctypes.data,
                                out["dv"].ctypes.data, out["lse"].ctypes.data,
                                out["delta"].ctypes.data)

@@ -451,11 +451,12 @@ bwa_status bwa_ring_bwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tens
   if ((s = check_scale(scale)) != BWA_OK) return s;
   if (mode == BWA_MODE_ROUNDS_TRANSFER)
     return fail(BWA_ERR_UNSUPPORTED, "ROUNDS_TRANSFER is a forward mode");
-  if (causal == 2) return fail(BWA_ERR_UNSUPPORTED, "striped causal order is forward only");
   if ((s = check_ring(q, k, n, mode)) != BWA_OK) return s;
   if ((s = check_sched(sched)) != BWA_OK) return s;
+  if (causal == 2 && q->S % n != 0)
+    return fail(BWA_ERR_UNSUPPORTED, "striped causal order needs n to divide S");
   if (!bwa::bwd_supported(q->dtype, (int)q->D))
-    return fail(BWA_ERR_UNSUPPORTED, "backward implemented for bf16, D = 128 only");
+    return fail(BWA_ERR_UNSUPPORTED, "backward implemented for bf16 only (D = 64 or 128)");
   if (q->S == 0) return BWA_OK;
   if (!lse) return fail(BWA_ERR_INVALID_ARG, "lse is NULL");
   const int64_t BH = q->B * q->H;
@@ -472,7 +473,7 @@ bwa_status bwa_ring_bwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tens
   a.n = n;
   a.sched = sched;
   a.mode = mode;
-  a.causal = causal ? 1 : 0;
+  a.causal = causal;
   a.scale = scale;
   a.workspace = workspace;
   hipError_t e = bwa::bwd_run(a, (hipStream_t)stream);

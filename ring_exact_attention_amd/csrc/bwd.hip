@@ -1,4 +1,4 @@
-// Backward of exact blockwise attention for gfx950 (bf16 inputs, D = 128).
+// Backward of exact blockwise attention for gfx950 (bf16 inputs, D = 64 or 128).
 //
 // The pages leave the distributed backward unspecified (LV-XAttn review,
 // referee report major comment 1, asks for exactly this: the gradient of the
@@ -39,8 +39,6 @@ struct BwdParams {
 
 namespace {
 
-constexpr int D = 128;
-
 __device__ inline uint32_t pk_bf16(float a, float b) {
   bf16 x = (bf16)a, y = (bf16)b;
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
@@ -67,11 +65,14 @@ __device__ inline int qblock_at_step(int sched, int n, int s, int r) {
 
 // ---------------------------------------------------------------- Delta = rowsum(dO * O)
 
+// D/8 consecutive threads per row, 8 elements each.
+template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
+  constexpr int TPR = D / 8;
   const int64_t rows = (int64_t)p.B * p.H * p.SQ;
   int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  int64_t row = idx / 16;
-  int c = (int)(idx % 16);
+  int64_t row = idx / TPR;
+  int c = (int)(idx % TPR);
   float s = 0.f;
   if (row < rows) {
     int64_t bh = row / p.SQ, i = row % p.SQ, b = bh / p.H, h = bh % p.H;
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
       s += __uint_as_float(o[w] & 0xffff0000u) * __uint_as_float(d[w] & 0xffff0000u);
     }
   }
-  s += __shfl_xor(s, 8);
+  if (TPR > 8) s += __shfl_xor(s, 8);
   s += __shfl_xor(s, 4);
   s += __shfl_xor(s, 2);
   s += __shfl_xor(s, 1);
@@ -91,13 +92,26 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
 }
 
 // LDS tiles of the two MFMA kernels below keep their rows in groups of four:
-// rows of a group 320 bytes apart (64 mod 256) and groups 1232 bytes apart
-// (16 mod 64).  Sixteen consecutive rows then start in sixteen distinct
-// 16-byte bank slots (row reads by ds_read_b128, one row per lane), and four
+// rows of a group 2(D+32) bytes apart (320 or 192: 64 or 192 mod 256) and
+// groups 2(4D+104) bytes apart (1232 or 720: 16 mod 64).  Sixteen consecutive
+// rows then start in sixteen distinct 16-byte bank slots (row reads by
+// ds_read_b128, one row per lane), and four
 // rows of a group cover all 64 banks with 64 bytes each (transposing reads by
 // ds_read_b64_tr_b16), while every address stays a lane base plus a constant.
-constexpr int kRowStr = D + 32, kGrpStr = 3 * kRowStr + D + 8;
-__device__ inline int rbase(int r) { return (r >> 2) * kGrpStr + (r & 3) * kRowStr; }
+template <int D>
+struct Lay {
+  static constexpr int kRowStr = D + 32, kGrpStr = 3 * kRowStr + D + 8;
+  __device__ static inline int rbase(int r) { return (r >> 2) * kGrpStr + (r & 3) * kRowStr; }
+  // A operand of 16 contraction rows (16t + 4g + {0..3}, 16t + 4g + 8 + {0..3};
+  // the row order of an MFMA result packed by pack8) x head dims 32dt + lane%32,
+  // read transposed from a row-major tile whose lane base is trb (below).
+  __device__ static inline bf16x8 tr_rows(const bf16* tile_lane, int t, int dt);
+  // Lane base of tr_rows: row 4g + li/4 (li = lane % 16), column 16*(lane/16 % 2) + 4*(li % 4).
+  __device__ static inline int trb(int lane) {
+    const int li = lane & 15, g = lane >> 5;
+    return g * kGrpStr + (li >> 2) * kRowStr + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
+  }
+};
 
 template <typename T>
 __device__ inline void hold(T& x) {  // materialise x here: an empty asm that reads and writes it
@@ -107,20 +121,13 @@ __device__ inline void hold(T& x) {  // materialise x here: an empty asm that re
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// A operand of 16 contraction rows (16t + 4g + {0..3}, 16t + 4g + 8 + {0..3};
-// the row order of an MFMA result packed by pack8) x head dims 32dt + lane%32,
-// read transposed from a row-major tile whose lane base is trb (below).
-__device__ inline bf16x8 tr_rows(const bf16* tile_lane, int t, int dt) {
+template <int D>
+__device__ inline bf16x8 Lay<D>::tr_rows(const bf16* tile_lane, int t, int dt) {
   const bf16* a0 = tile_lane + 4 * t * kGrpStr + 32 * dt;
   s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
   s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0 + 2 * kGrpStr));
   u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
   return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
-}
-// Lane base of tr_rows: row 4g + li/4 (li = lane % 16), column 16*(lane/16 % 2) + 4*(li % 4).
-__device__ inline int trb(int lane) {
-  const int li = lane & 15, g = lane >> 5;
-  return g * kGrpStr + (li >> 2) * kRowStr + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
 }
 
 // ---------------------------------------------------------------- dK, dV (KV-stationary)
@@ -146,9 +153,18 @@ __device__ inline int trb(int lane) {
 // dK/dV: 8 waves in two roles; dQ: 8 waves, two per SIMD.
 constexpr int kDkdvWaves = 8, kDqWaves = 8;
 
-// CAUSAL instantiates the masking code; p.causal must agree.
-template <bool CAUSAL>
+// CM instantiates the masking code (0 none, 1 sequence order, 2 striped
+// order); p.causal must agree.  Under either causal order a key sees the
+// query rows of a segment from a first row on: key row j from row j (sequence
+// order); in the striped order, key index c of shard s from index c of query
+// shards w >= s and index c + 1 of shards w < s (its position is c*n + s).
+// With qo = (query shard start) - (key shard start) + [s > w] (0 in sequence
+// order) the first row that sees key j is j + qo.
+template <int D, int CM>
 __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) {
+  constexpr bool CAUSAL = CM != 0;
+  using Ly = Lay<D>;
+  constexpr int kGrpStr = Ly::kGrpStr;
   constexpr int BK = 128, BQ = 64, GT = 64 * kDkdvWaves / 2;
   constexpr int TILE = BQ / 4 * kGrpStr, STAGE = 2 * TILE, NBUF = 3;
   constexpr int KC = (BQ * D / 8) / GT;  // 16-byte chunks per staging thread and tile
@@ -202,19 +218,21 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
   struct It {
     int r;
     int64_t qt, qe;
+    int qo;  // causal: the first query row that sees key j is j + qo
   };
   auto seek = [&](It& it, int from) {
     for (it.r = from; it.r < nseg; ++it.r) {
       int qb = fixed_qb >= 0 ? fixed_qb : qblock_at_step(p.sched, p.n, shard, it.r);
       int64_t a = shard_start(p.SQ, p.n, qb), e = shard_start(p.SQ, p.n, qb + 1);
-      if (p.causal && a < kt0) a = kt0;  // queries before the tile's first key see none of it
+      it.qo = CM == 2 ? (int)(a - ks) + (shard > qb ? 1 : 0) : 0;
+      if (CAUSAL && a < kt0 + it.qo) a = kt0 + it.qo;  // rows before that see none of the tile
       if (e > a) {
         it.qt = a;
         it.qe = e;
         return;
       }
     }
-    it.qt = it.qe = 0;
+    it.qt = it.qe = it.qo = 0;
   };
   auto advance = [&](It& it) {
     it.qt += BQ;
@@ -261,7 +279,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
         st_d = gtid < lim ? dltg[row] : 0.f;
     }
   };
-  const int wbase = soff + rbase(srow0) + scol * 8;
+  const int wbase = soff + Ly::rbase(srow0) + scol * 8;
   auto store_tile = [&](int buf) {
     bf16* dst = smem + buf * STAGE + wbase;
 #pragma unroll
@@ -276,8 +294,8 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
 
   f32x16 sacc[BQ / 32], pacc[BQ / 32];
   bf16x8 xb[BQ / 16];  // P (A) or dS (B) of the last VALU phase, bf16, in MFMA B-operand order
-  const int rb = rbase(lr) + 8 * g;  // this lane's row-read base
-  const int tb = trb(lane);
+  const int rb = Ly::rbase(lr) + 8 * g;  // this lane's row-read base
+  const int tb = Ly::trb(lane);
   // One MFMA slot as a fixed sequence: dV or dK of the current tile (16
   // MFMAs), then S (A) or dP (B) of the next (16).  The A operand of MFMA
   // m + DIST is read from LDS just before MFMA m is issued and a scheduling
@@ -304,7 +322,7 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
     auto rd = [&](auto M) -> bf16x8 {
       constexpr int m = decltype(M)::value;
       if constexpr (m < NACC) {  // dV: dO^T from the dO half; dK: Q^T from the Q half
-        return tr_rows(smem + cur_buf * STAGE + (RB ? 0 : TILE) + tb, m / (D / 32), m % (D / 32));
+        return Ly::tr_rows(smem + cur_buf * STAGE + (RB ? 0 : TILE) + tb, m / (D / 32), m % (D / 32));
       } else {  // S: Q rows; dP: dO rows
         constexpr int q = m - NACC, s = q / (BQ / 32), u = q % (BQ / 32);
         return *(const bf16x8*)(smem + nxt_buf * STAGE + (RB ? TILE : 0) + rb + u * 8 * kGrpStr +
@@ -358,9 +376,10 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
   auto phase_valu = [&](auto ROLE_B, const It& t) {
     constexpr bool RB = decltype(ROLE_B)::value;
     if constexpr (!RB) {
-      const bool need_mask = CAUSAL && t.qt < kw0 + 31;
+      const bool need_mask = CAUSAL && t.qt < kw0 + t.qo + 31;
       // query offsets below lim precede this lane's key: no weight
-      const int lim = need_mask ? (int)max(min(mykey - t.qt, (int64_t)BQ), (int64_t)0) : 0;
+      const int lim =
+          need_mask ? (int)max(min(mykey + t.qo - t.qt, (int64_t)BQ), (int64_t)0) : 0;
 #pragma unroll
       for (int u = 0; u < BQ / 32; ++u) {
 #pragma unroll
@@ -502,8 +521,17 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
 // group A's S/dP of that tile.  Tiles rotate through three LDS buffers; each
 // half of a buffer is rewritten only after its last reader's slot.
 
-template <bool CAUSAL>
+// CM as in the dK/dV kernel.  Under either causal order a query row sees the
+// keys of a segment up to a last key: row i up to key i (sequence order); in
+// the striped order, the row at index c of query shard w sees indices up to c
+// of key shards s <= w and up to c - 1 of shards s > w.  With ko = (key shard
+// start) - (query shard start) - [s > w] (0 in sequence order) the last key
+// row that query row i sees is i + ko.
+template <int D, int CM>
 __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdParams p) {
+  constexpr bool CAUSAL = CM != 0;
+  using Ly = Lay<D>;
+  constexpr int kGrpStr = Ly::kGrpStr;
   constexpr int BM = 32 * kDqWaves, BN = 64, GT = 64 * kDqWaves / 2;
   constexpr int TILE = BN / 4 * kGrpStr, STAGE = 2 * TILE, NBUF = 3;
   constexpr int KC = (BN * D / 8) / GT;  // 16-byte chunks per staging thread and tile
@@ -566,19 +594,21 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdParams p) {
   struct It {
     int r;
     int64_t kt, ke;
+    int ko;  // causal: the last key row that query row i sees is i + ko
   };
   auto seek = [&](It& it, int from) {
     for (it.r = from; it.r < nseg; ++it.r) {
       int kb = fixed_kb >= 0 ? fixed_kb : shard_at_step(p.sched, p.n, j, it.r);
       int64_t a = shard_start(p.SKV, p.n, kb), e = shard_start(p.SKV, p.n, kb + 1);
-      if (p.causal && e > r1) e = r1;
+      it.ko = CM == 2 ? (int)(a - qs) - (kb > j ? 1 : 0) : 0;
+      if (CAUSAL && e > r1 + it.ko) e = r1 + it.ko;  // keys after the job's last row's last key
       if (e > a) {
         it.kt = a;
         it.ke = e;
         return;
       }
     }
-    it.kt = it.ke = 0;
+    it.kt = it.ke = it.ko = 0;
   };
   auto advance = [&](It& it) {
     it.kt += BN;
@@ -616,7 +646,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdParams p) {
     }
   };
   static_assert(srstep % 4 == 0, "staging rows keep their place in a row group");
-  const int wbase = soff + rbase(srow0) + scol * 8;
+  const int wbase = soff + Ly::rbase(srow0) + scol * 8;
   auto store_tile = [&](int buf) {
     bf16* dst = smem + buf * STAGE + wbase;
 #pragma unroll
@@ -627,7 +657,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdParams p) {
   f32x16 sacc[BN / 32], pacc[BN / 32];
   bf16x8 dsb[BN / 16];
   // S^T = K Q^T and dP^T = V dO^T; element 4i+jj of block u is key 32u+8i+4g+jj
-  const int rb = rbase(lr) + 8 * g;  // this lane's row-read base
+  const int rb = Ly::rbase(lr) + 8 * g;  // this lane's row-read base
   auto phase_sdp = [&](int buf) {
     const bf16* ks = smem + buf * STAGE + rb;
     const bf16* vs = ks + TILE;
@@ -646,7 +676,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdParams p) {
   };
   // dQ^T += K^T dS^T: the A operand of step t covers keys 16t+4g+{0..3} and
   // 16t+4g+8+{0..3} of head dims 32dt + lane%32, the key order of dsb[t]
-  const int tb = trb(lane);
+  const int tb = Ly::trb(lane);
   // One MFMA slot as a fixed sequence: dQ of the current tile (16 MFMAs), then
   // S and dP of the next (32).  The A operand of MFMA m + DIST is read from
   // LDS just before MFMA m is issued and a scheduling barrier follows every
@@ -656,7 +686,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdParams p) {
   auto op_read = [&](auto M, int cur_buf, int nxt_buf) -> bf16x8 {
     constexpr int m = decltype(M)::value;
     if constexpr (m < NDQ) {
-      return tr_rows(smem + cur_buf * STAGE + tb, m / (D / 32), m % (D / 32));
+      return Ly::tr_rows(smem + cur_buf * STAGE + tb, m / (D / 32), m % (D / 32));
     } else {
       constexpr int q = m - NDQ, s = q / 4, u = (q / 2) % 2, kind = q % 2;
       return *(const bf16x8*)(smem + nxt_buf * STAGE + kind * TILE + rb + u * 8 * kGrpStr + 16 * s);
@@ -692,8 +722,9 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdParams p) {
   auto phase_ds = [&](const It& t) {
     // causal: this row sees keys kt .. kt+lim-1 of the tile (keys past the
     // segment end have zero K rows, see load_tile)
-    const bool need_mask = CAUSAL && t.kt + BN - 1 > wrow0;
-    const int lim = need_mask ? (int)max(min(myrow + 1 - t.kt, (int64_t)BN), (int64_t)0) : BN;
+    const bool need_mask = CAUSAL && t.kt + BN - 1 > wrow0 + t.ko;
+    const int lim =
+        need_mask ? (int)max(min(myrow + t.ko + 1 - t.kt, (int64_t)BN), (int64_t)0) : BN;
 #pragma unroll
     for (int u = 0; u < BN / 32; ++u)
 #pragma unroll
@@ -803,6 +834,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdParams p) {
 }
 
 // fp32 [BH][S][D] accumulator -> bf16 tensor (ROUNDS mode, after the last round).
+template <int D>
 __global__ __launch_bounds__(256) void bwd_convert_kernel(const float* acc, bf16* out, int B,
                                                           int H, int S, int64_t s0, int64_t s1,
                                                           int64_t s2) {
@@ -818,7 +850,7 @@ __global__ __launch_bounds__(256) void bwd_convert_kernel(const float* acc, bf16
 
 // ---------------------------------------------------------------- host side
 
-bool bwd_supported(int dtype, int Dh) { return dtype == 1 && Dh == D; }
+bool bwd_supported(int dtype, int Dh) { return dtype == 1 && (Dh == 64 || Dh == 128); }
 
 static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -834,6 +866,53 @@ static void strides(const bwa_tensor* t, int64_t* s) {
   s[0] = t->sB;
   s[1] = t->sH;
   s[2] = t->sS;
+}
+
+// The launches of one backward pass for head dim D and causal order CM.
+template <int D, int CM>
+static hipError_t bwd_launch_all(BwdParams p, hipStream_t st) {
+  const int64_t BH = (int64_t)p.B * p.H;
+  int64_t nthr = BH * p.SQ * (D / 8);
+  hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, st,
+                     p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const int BK = 128, BM = 32 * kDqWaves;
+  const int kv_tiles = (int)(((p.SKV + p.n - 1) / p.n + BK - 1) / BK);
+  const int q_tiles = (int)(((p.SQ + p.n - 1) / p.n + BM - 1) / BM);
+  const int groups = (int)(BH * p.n);
+  const int rounds = p.mode == MODE_ROUNDS ? p.n : 1;
+  for (int r = 0; r < rounds; ++r) {
+    p.round = r;
+    p.groups = groups;
+    p.tiles = kv_tiles;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CM>), dim3(xcd_grid_size(kv_tiles, groups)),
+                       dim3(64 * kDkdvWaves), 0, st, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    p.tiles = q_tiles;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CM>), dim3(xcd_grid_size(q_tiles, groups)),
+                       dim3(64 * kDqWaves), 0, st, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (p.mode == MODE_ROUNDS) {
+    int64_t tq = BH * p.SQ * (D / 4), tk = BH * p.SKV * (D / 4);
+    hipLaunchKernelGGL(bwd_convert_kernel<D>, dim3((unsigned)((tq + 255) / 256)), dim3(256), 0, st,
+                       p.dq_acc, p.dq, p.B, p.H, p.SQ, p.sdq[0], p.sdq[1], p.sdq[2]);
+    hipLaunchKernelGGL(bwd_convert_kernel<D>, dim3((unsigned)((tk + 255) / 256)), dim3(256), 0, st,
+                       p.dk_acc, p.dk, p.B, p.H, p.SKV, p.sdk[0], p.sdk[1], p.sdk[2]);
+    hipLaunchKernelGGL(bwd_convert_kernel<D>, dim3((unsigned)((tk + 255) / 256)), dim3(256), 0, st,
+                       p.dv_acc, p.dv, p.B, p.H, p.SKV, p.sdv[0], p.sdv[1], p.sdv[2]);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+template <int D>
+static hipError_t bwd_launch_d(const BwdParams& p, hipStream_t st) {
+  if (p.causal == 2) return bwd_launch_all<D, 2>(p, st);
+  if (p.causal == 1) return bwd_launch_all<D, 1>(p, st);
+  return bwd_launch_all<D, 0>(p, st);
 }
 
 hipError_t bwd_run(const BwdArgs& a, hipStream_t st) {
@@ -865,59 +944,19 @@ hipError_t bwd_run(const BwdArgs& a, hipStream_t st) {
   p.causal = a.causal;
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
+  const int Dh = (int)a.q->D;
   const int64_t BH = (int64_t)p.B * p.H;
   char* ws = (char*)a.workspace;
   p.delta = (float*)ws;
   ws += a256((size_t)BH * p.SQ * 4);
   if (p.mode == MODE_ROUNDS) {
     p.dq_acc = (float*)ws;
-    ws += a256((size_t)BH * p.SQ * D * 4);
+    ws += a256((size_t)BH * p.SQ * Dh * 4);
     p.dk_acc = (float*)ws;
-    ws += a256((size_t)BH * p.SKV * D * 4);
+    ws += a256((size_t)BH * p.SKV * Dh * 4);
     p.dv_acc = (float*)ws;
   }
-
-  int64_t nthr = BH * p.SQ * 16;
-  hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, st, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
-  const int BK = 128, BM = 32 * kDqWaves;
-  const int kv_tiles = (int)(((p.SKV + p.n - 1) / p.n + BK - 1) / BK);
-  const int q_tiles = (int)(((p.SQ + p.n - 1) / p.n + BM - 1) / BM);
-  const int groups = (int)(BH * p.n);
-  const int rounds = p.mode == MODE_ROUNDS ? p.n : 1;
-  for (int r = 0; r < rounds; ++r) {
-    p.round = r;
-    p.groups = groups;
-    p.tiles = kv_tiles;
-    if (p.causal)
-      hipLaunchKernelGGL(bwd_dkdv_kernel<true>, dim3(xcd_grid_size(kv_tiles, groups)),
-                         dim3(64 * kDkdvWaves), 0, st, p);
-    else
-      hipLaunchKernelGGL(bwd_dkdv_kernel<false>, dim3(xcd_grid_size(kv_tiles, groups)),
-                         dim3(64 * kDkdvWaves), 0, st, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    p.tiles = q_tiles;
-    if (p.causal)
-      hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3(xcd_grid_size(q_tiles, groups)),
-                         dim3(64 * kDqWaves), 0, st, p);
-    else
-      hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3(xcd_grid_size(q_tiles, groups)),
-                         dim3(64 * kDqWaves), 0, st, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  if (p.mode == MODE_ROUNDS) {
-    int64_t tq = BH * p.SQ * (D / 4), tk = BH * p.SKV * (D / 4);
-    hipLaunchKernelGGL(bwd_convert_kernel, dim3((unsigned)((tq + 255) / 256)), dim3(256), 0, st,
-                       p.dq_acc, p.dq, p.B, p.H, p.SQ, p.sdq[0], p.sdq[1], p.sdq[2]);
-    hipLaunchKernelGGL(bwd_convert_kernel, dim3((unsigned)((tk + 255) / 256)), dim3(256), 0, st,
-                       p.dk_acc, p.dk, p.B, p.H, p.SKV, p.sdk[0], p.sdk[1], p.sdk[2]);
-    hipLaunchKernelGGL(bwd_convert_kernel, dim3((unsigned)((tk + 255) / 256)), dim3(256), 0, st,
-                       p.dv_acc, p.dv, p.B, p.H, p.SKV, p.sdv[0], p.sdv[1], p.sdv[2]);
-    e = hipGetLastError();
-  }
-  return e;
+  return Dh == 64 ? bwd_launch_d<64>(p, st) : bwd_launch_d<128>(p, st);
 }
 
 }  // namespace bwa

@@ -165,6 +165,11 @@ def test_ring_bwd_validation(L):
     a = [ctypes.byref(x) for x in (qf, kf, kf, qf)] + [FAKE, ctypes.byref(qf), 4, 0, 1, 0, 0.1] + \
         [ctypes.byref(x) for x in (qf, kf, kf)] + [None, 0, None]
     expect(L, L.bwa_ring_bwd(*a), _bwa.BWA_ERR_UNSUPPORTED, "backward")
+    # striped causal order: self-attention with n dividing S
+    s = T(S=300)
+    a = [ctypes.byref(x) for x in (s, s, s, s)] + [FAKE, ctypes.byref(s), 7, 0, 1, 2, 0.1] + \
+        [ctypes.byref(x) for x in (s, s, s)] + [None, 0, None]
+    expect(L, L.bwa_ring_bwd(*a), _bwa.BWA_ERR_UNSUPPORTED, "divide")
 
 
 def test_kv_recompute_validation(L):

@@ -33,23 +33,33 @@ def gen(B, H, SQ, SKV, D, seed, std=0.5):
 
 
 BWD_SHAPES = [
-    # B, H, SQ, SKV, n, causal
-    (1, 2, 256, 1024, 4, False),
-    (1, 2, 300, 1000, 4, False),   # ragged tiles and shards
-    (2, 1, 65, 130, 3, False),
-    (1, 1, 5, 100, 8, False),      # empty query blocks
-    (1, 2, 512, 512, 4, True),
-    (1, 1, 300, 300, 3, True),
+    # B, H, SQ, SKV, n, causal, D
+    (1, 2, 256, 1024, 4, False, 128),
+    (1, 2, 300, 1000, 4, False, 128),    # ragged tiles and shards
+    (2, 1, 65, 130, 3, False, 128),
+    (1, 1, 5, 100, 8, False, 128),       # empty query blocks
+    (1, 2, 512, 512, 4, True, 128),
+    (1, 1, 300, 300, 3, True, 128),
+    (1, 2, 300, 1000, 4, False, 64),     # D = 64
+    (2, 1, 65, 130, 3, False, 64),
+    (1, 2, 512, 512, 4, True, 64),
+    (1, 1, 300, 300, 3, True, 64),
+    # rows in the striped order over the n shards (n divides S)
+    (1, 2, 512, 512, 4, "striped", 128),
+    (1, 1, 384, 384, 3, "striped", 128),  # shards of 128: key tiles end on shard ends
+    (1, 1, 300, 300, 5, "striped", 128),  # shards of 60: ragged tiles inside each shard
+    (2, 1, 1024, 1024, 8, "striped", 128),
+    (1, 2, 384, 384, 3, "striped", 64),
 ]
 
 
 @pytest.mark.parametrize("shape", BWD_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_bwd_small(bwa, orc, shape):
-    B, H, SQ, SKV, n, causal = shape
-    D = 128
+    B, H, SQ, SKV, n, causal, D = shape
     scale = 1 / math.sqrt(D)
-    q, k, v, do = gen(B, H, SQ, SKV, D, seed=SQ + SKV)
-    ref = orc.attn_bwd(q, k, v, do, scale, causal)
+    q, k, v, do = gen(B, H, SQ, SKV, D, seed=SQ + SKV + D)
+    oc = ("striped", n) if causal == "striped" else causal
+    ref = orc.attn_bwd(q, k, v, do, scale, oc)
     qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
     o, lse = bwa.bwa_ring_fwd(qd, kd, vd, n, "kv", "fused", causal=causal, scale=scale)
     for mode in ("fused", "rounds"):
