@@ -7,10 +7,15 @@ A step is one whole ring forward (every round of the schedule, every block
 pair, the merge and the final output) over inputs already resident in HBM.
 
 Prints one JSON line.  `value` is attention TFLOP/s counted as
-4 * B * H * S_Q * S_KV * D per step.  `roofline` reports the dominant kernel
-against the dense bf16 MFMA peak (2.5 PFLOP/s), its duration measured with
-HIP events on the stream the library launches on.  `cpu_baseline` times the
-fp64 CPU oracle on a bounded sample of the same workload.
+4 * B * H * S_Q * S_KV * D per step, from the median step time (min, max and
+mean are reported beside it).  `roofline` reports the dominant kernel against
+its bound: the dense bf16 MFMA peak (2.5 PFLOP/s) for the compute-bound
+workloads, HBM (8 TB/s) for the short-query one, with the kernel's duration
+measured with HIP events on the stream the library launches on.  Counter
+summaries committed under profiles/ (HBM bytes, MFMA busy fraction, running
+clock) are attached when they were taken on the current kernel source.
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -27,8 +32,23 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+NOMINAL_CLOCK_GHZ = 2.4
+SIMDS = 256 * 4  # compute units x SIMDs per CU
 METRIC = "attention TFLOP/s and % bf16 MFMA peak, S_Q=2K x S_KV=128K d=128, 1 GPU"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_lvx_2k_128k_traffic.txt")
+PROFILES = os.path.join(ROOT, "profiles")
+# the forward workloads' bound; the rest are compute-bound
+HBM_BOUND = {"shortq_256_256k"}
+# default ring mode per workload: split everywhere except causal self-attention,
+# where split would write n fp32 partials of the whole sequence
+DEFAULT_MODE = {"causal_64k": "fused"}
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"fwd_bf16_{workload}_traffic.txt")
+
+
+def counters_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"mfma_busy_{workload}.txt")
 
 
 def kernel_source_hash() -> str:
@@ -39,22 +59,38 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(mode: str):
+def _read_kv(path: str) -> dict:
+    kv = {}
+    if os.path.exists(path):
+        for line in open(path):
+            if "=" in line and not line.lstrip().startswith("#"):
+                a, b = line.split("=", 1)
+                kv[a.strip()] = b.strip()
+    return kv
+
+
+def read_traffic(workload: str, mode: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source and the same mode; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    kv = {}
-    for line in open(TRAFFIC_FILE):
-        if "=" in line and not line.lstrip().startswith("#"):
-            a, b = line.split("=", 1)
-            kv[a.strip()] = b.strip()
+    kv = _read_kv(traffic_file(workload))
     if kv.get("kernel_hash") != kernel_source_hash() or kv.get("mode") != mode:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def read_counters(workload: str, mode: str):
+    """(MFMA busy fraction, clock GHz) of the forward kernel from the committed
+    counter summary, if taken on the current kernel source and mode."""
+    kv = _read_kv(counters_file(workload))
+    if kv.get("kernel_hash") != kernel_source_hash() or kv.get("mode") != mode:
+        return None, None
+    try:
+        return float(kv["fwd_mfma_busy"]), float(kv["fwd_clock_ghz"])
+    except (KeyError, ValueError):
+        return None, None
 
 
 def cpu_baseline(q, k, v, w, rows_per_head: int):
@@ -85,7 +121,8 @@ def _find(d: str, suffix: str) -> str:
     raise FileNotFoundError(f"no *{suffix} under {d}")
 
 
-def summarize_traffic(fetch_dir: str, write_dir: str, mode: str, command: str) -> str:
+def summarize_traffic(fetch_dir: str, write_dir: str, workload: str, mode: str,
+                      command: str) -> str:
     """Write the committed HBM-traffic summary from two rocprofv3 counter passes
     (FETCH_SIZE, then WRITE_SIZE) of `bench.py --copy-calibration`.  Each counter
     is scaled by what it reads for the 1 GiB copy kernel of the same run."""
@@ -107,17 +144,18 @@ def summarize_traffic(fetch_dir: str, write_dir: str, mode: str, command: str) -
     f_kib = sum(fe[kk][1:]) / len(fe[kk][1:])  # the first launch is a warm-up
     w_kib = sum(wr[kk][1:]) / len(wr[kk][1:])
     fetch_b, write_b = f_kib * 1024 * f_factor, w_kib * 1024 * w_factor
-    text = f"""# HBM traffic per launch of {kk} (workload lvx_2k_128k, mode {mode})
+    text = f"""# HBM traffic per launch of {kk} (workload {workload}, mode {mode})
 # from two rocprofv3 counter passes (FETCH_SIZE, then WRITE_SIZE), KiB per dispatch,
 # each scaled by what the same counter reads for a plain 1 GiB copy kernel
 # (dst.copy_(src) of 2^29 bf16 elements, run by --copy-calibration in the same process).
 # commands (from /tmp, one pass each; then this file is written by
-#   python bench.py --mode {mode} --summarize-traffic <fetch_dir> <write_dir>):
+#   python bench.py --workload {workload} --mode {mode} --summarize-traffic <fetch_dir> <write_dir>):
 #   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -o run -- {command}
 #   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -o run -- {command}
 # raw: FETCH_SIZE {f_kib:.0f} KiB/launch; copy kernel FETCH_SIZE {fe[ck][0]:.0f} KiB for 1048576 KiB moved
 #      WRITE_SIZE {w_kib:.0f} KiB/launch; copy kernel WRITE_SIZE {wr[ck][0]:.0f} KiB for 1048576 KiB moved
 kernel={kk}
+workload={workload}
 mode={mode}
 kernel_hash={kernel_source_hash()}
 fetch_factor={f_factor:.4f}
@@ -126,25 +164,142 @@ fetch_bytes_per_launch={fetch_b:.0f}
 write_bytes_per_launch={write_b:.0f}
 hbm_bytes_per_launch={fetch_b + write_b:.0f}
 """
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(traffic_file(workload), "w") as f:
         f.write(text)
     return text
 
 
-def summarize_stats(stats_dir: str, workload: str, command: str, top: int = 8) -> str:
-    """Write profiles/kernels_<workload>.txt from a rocprofv3 --kernel-trace --stats run."""
+def _bench_line(log: str) -> dict:
+    """The JSON line bench.py printed into `log`."""
+    for line in open(log):
+        line = line.strip()
+        if line.startswith("{") and '"metric"' in line:
+            return json.loads(line)
+    raise ValueError(f"no bench JSON line in {log}")
+
+
+def _short(name: str) -> str:
+    name = name.replace("void ", "").replace("bwa::", "")
+    return name.split("(")[0][:60]
+
+
+def _trace_rows(trace_dir: str):
+    """(kernel name, duration ns, start ns) of every dispatch, in launch order."""
     import csv
-    rows = list(csv.DictReader(open(_find(stats_dir, "kernel_stats.csv"))))
-    lines = [f"# rocprofv3 kernel statistics, workload {workload}",
-             f"# command (from /tmp): rocprofv3 --kernel-trace --stats --output-format csv "
-             f"-d <dir> -o run -- {command}",
-             "# columns: calls, average us, total ms, percent of GPU time, kernel"]
-    for r in rows[:top]:
-        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:12.1f} "
-                     f"{float(r['TotalDurationNs']) / 1e6:10.3f} {float(r['Percentage']):6.2f}  "
-                     f"{r['Name'][:160]}")
+    rows = [(r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
+             int(r["Start_Timestamp"]))
+            for r in csv.DictReader(open(_find(trace_dir, "kernel_trace.csv")))]
+    rows.sort(key=lambda x: x[2])
+    return rows
+
+
+def summarize_stats(trace_dir: str, bench_log: str, name: str, command: str) -> str:
+    """Write profiles/kernels_<name>.txt from a rocprofv3 --kernel-trace run of
+    bench.py: per kernel, the average over the timed steps only (the first
+    `warmup` steps' dispatches of each kernel are left out; they run at lower
+    clocks), beside the median step time bench.py measured in that same run."""
+    import collections
+    b = _bench_line(bench_log)
+    steps, warm = b["steps"], b["warmup"]
+    per = collections.defaultdict(list)
+    for k, dur, _ in _trace_rows(trace_dir):
+        per[k].append(dur)
+    lines = [f"# rocprofv3 kernel trace, workload {name}; averages over the {steps} timed steps",
+             f"# (the first {warm} warm-up steps' dispatches of every kernel are left out)",
+             f"# command (from /tmp): rocprofv3 --kernel-trace --output-format csv -d <dir> -o run "
+             f"-- {command}",
+             f"# the same run's bench.py line: ms_per_step (median) {b['ms_per_step']}, "
+             f"min {b.get('ms_per_step_min')}, max {b.get('ms_per_step_max')}, "
+             f"value {b['value']} {b['unit']}",
+             "# columns: dispatches per step, average us, min us, max us, ms per step, kernel"]
+    out = []
+    for k, durs in per.items():
+        if k.startswith("__amd") or "copyBuffer" in k or "fillBuffer" in k or "elementwise" in k:
+            continue
+        per_step = len(durs) // (steps + warm) if len(durs) >= steps + warm else 0
+        if per_step == 0:
+            continue
+        timed = durs[warm * per_step:(warm + steps) * per_step]
+        avg = sum(timed) / len(timed)
+        out.append((avg * per_step, per_step, avg, min(timed), max(timed), k))
+    out.sort(reverse=True)
+    for tot, per_step, avg, lo, hi, k in out:
+        lines.append(f"{per_step:4d} {avg / 1e3:10.1f} {lo / 1e3:10.1f} {hi / 1e3:10.1f} "
+                     f"{tot / 1e6:8.3f}  {_short(k)}")
     text = "\n".join(lines) + "\n"
-    with open(os.path.join(ROOT, "profiles", f"kernels_{workload}.txt"), "w") as f:
+    with open(os.path.join(PROFILES, f"kernels_{name}.txt"), "w") as f:
+        f.write(text)
+    return text
+
+
+def summarize_counters(pmc_dir: str, bench_log: str, name: str, command: str) -> str:
+    """Write profiles/mfma_busy_<name>.txt from a rocprofv3 --pmc run with
+    --kernel-trace: per kernel, over the timed steps' dispatches,
+      MFMA busy = MfmaUtil / 100 = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs),
+      clock     = cycles / duration,
+    with cycles the GRBM_GUI_ACTIVE of the busiest XCD (recovered from
+    MfmaUtil and the summed busy cycles; without MfmaUtil, the XCD-summed
+    GRBM_GUI_ACTIVE / 8), and the bf16 MFMA work the kernel executed,
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 FLOP."""
+    import collections
+    import csv
+    b = _bench_line(bench_log)
+    steps, warm = b["steps"], b["warmup"]
+    vals = collections.defaultdict(lambda: collections.defaultdict(float))
+    names, starts = {}, {}
+    for r in csv.DictReader(open(_find(pmc_dir, "counter_collection.csv"))):
+        d = int(r["Dispatch_Id"])
+        vals[d][r["Counter_Name"]] += float(r["Counter_Value"])
+        names[d] = r["Kernel_Name"]
+    durs = {}
+    for r in csv.DictReader(open(_find(pmc_dir, "kernel_trace.csv"))):
+        d = int(r["Dispatch_Id"])
+        durs[d] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        starts[d] = int(r["Start_Timestamp"])
+    per = collections.defaultdict(list)
+    for d in sorted(vals, key=lambda x: starts.get(x, x)):
+        if d in durs:
+            per[names[d]].append((durs[d], vals[d]))
+    lines = [f"# rocprofv3 counters per kernel, workload {name}; averages over the {steps} timed",
+             f"# steps (warm-up dispatches left out).  MFMA busy = rocprofv3's MfmaUtil, i.e.",
+             f"# SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs) with cycles the busiest XCD's",
+             f"# GRBM_GUI_ACTIVE; clock = cycles / duration; executed TFLOP =",
+             f"# SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512.",
+             f"# command (from /tmp): rocprofv3 --kernel-trace --pmc MfmaUtil "
+             f"SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+             f"--output-format csv -d <dir> -o run -- {command}",
+             f"# the same run's bench.py line: ms_per_step (median) {b['ms_per_step']}",
+             "# columns: dispatches per step, average us, clock GHz, MFMA busy, executed bf16 "
+             "TFLOP per dispatch, executed TFLOP/s, kernel"]
+    kv = {}
+    for k, recs in per.items():
+        per_step = len(recs) // (steps + warm) if len(recs) >= steps + warm else 0
+        if per_step == 0 or k.startswith("__amd") or "copyBuffer" in k:
+            continue
+        timed = recs[warm * per_step:(warm + steps) * per_step]
+        dur = sum(x[0] for x in timed) / len(timed)
+        busy = sum(x[1].get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for x in timed) / len(timed)
+        mops = sum(x[1].get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) for x in timed) / len(timed)
+        util = [x[1]["MfmaUtil"] for x in timed if "MfmaUtil" in x[1]]
+        if util and busy > 0:
+            # MfmaUtil divides by the busiest XCD's GRBM_GUI_ACTIVE: recover those cycles
+            frac = sum(util) / len(util) / 100.0
+            cyc = busy / (frac * SIMDS) if frac > 0 else 0.0
+        else:
+            cyc = sum(x[1].get("GRBM_GUI_ACTIVE", 0.0) for x in timed) / len(timed) / 8
+            frac = busy / (cyc * SIMDS) if cyc else 0.0
+        clock = cyc / dur if dur else 0.0
+        tflop = mops * 512 / 1e12
+        lines.append(f"{per_step:4d} {dur / 1e3:10.1f} {clock:6.3f} {frac:6.3f} {tflop:8.4f} "
+                     f"{tflop / (dur * 1e-9) if dur else 0:9.1f}  {_short(k)}")
+        if "fwd_bf16_kernel" in k:
+            kv = {"fwd_mfma_busy": f"{frac:.4f}", "fwd_clock_ghz": f"{clock:.4f}",
+                  "fwd_avg_us": f"{dur / 1e3:.1f}"}
+    if kv:
+        lines += [f"kernel_hash={kernel_source_hash()}", f"mode={b['config'].get('mode')}"]
+        lines += [f"{a}={v}" for a, v in kv.items()]
+    text = "\n".join(lines) + "\n"
+    with open(counters_file(name), "w") as f:
         f.write(text)
     return text
 
@@ -169,14 +324,40 @@ def summarize_rounds(trace_dirs, labels, workload: str, n: int, command: str) ->
     return text
 
 
+def summarize_sweep(logs, command: str) -> str:
+    """Write profiles/sweep_sq_lvx_2k_128k.txt from bench.py lines of the
+    headline workload at several S_Q (same S_KV, heads, D, shards)."""
+    rows = sorted((_bench_line(f) for f in logs), key=lambda b: b["config"]["S_Q"])
+    base = rows[0]
+    lines = ["# S_Q sweep at S_KV = 131072, 32 heads, D = 128, n = 8, split mode: the block",
+             "# attention's time against the query length at fixed KV length (time grows in",
+             "# proportion to S_Q when the path is compute-bound, stays flat when KV streaming",
+             "# dominates).",
+             f"# command per point: {command} --sq <S_Q>",
+             "# columns: S_Q, median ms per step, TFLOP/s, frac of bf16 peak, ms / (ms at the "
+             "smallest S_Q) / (S_Q / smallest S_Q)"]
+    for b in rows:
+        r = (b["ms_per_step"] / base["ms_per_step"]) / (b["config"]["S_Q"] / base["config"]["S_Q"])
+        lines.append(f"{b['config']['S_Q']:6d} {b['ms_per_step']:8.3f} {b['value']:8.1f} "
+                     f"{b['value'] / PEAK_BF16_TFLOPS:6.3f} {r:6.3f}")
+    text = "\n".join(lines) + "\n"
+    with open(os.path.join(PROFILES, "sweep_sq_lvx_2k_128k.txt"), "w") as f:
+        f.write(text)
+    return text
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="lvx_2k_128k")
-    ap.add_argument("--mode", default="split", choices=["rounds", "fused", "split", "rounds_transfer"])
+    ap.add_argument("--mode", default=None,
+                    choices=["rounds", "fused", "split", "rounds_transfer"],
+                    help="ring mode (default: fused for causal self-attention, else split)")
     ap.add_argument("--sched", default="kv", choices=["kv", "q"])
+    ap.add_argument("--sq", type=int, default=None,
+                    help="override the workload's query length (S_Q sweep)")
     ap.add_argument("--cpu-rows-per-head", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--striped", action="store_true",
@@ -191,17 +372,27 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ traffic summary from two rocprofv3 counter passes "
                          "and exit (no GPU use)")
-    ap.add_argument("--summarize-stats", metavar="STATS_DIR",
-                    help="write profiles/kernels_<workload>.txt from a rocprofv3 --stats run "
-                         "and exit (no GPU use)")
+    ap.add_argument("--summarize-stats", nargs=2, metavar=("TRACE_DIR", "BENCH_LOG"),
+                    help="write profiles/kernels_<workload>.txt from a rocprofv3 --kernel-trace "
+                         "run and the bench line it printed, and exit (no GPU use)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("PMC_DIR", "BENCH_LOG"),
+                    help="write profiles/mfma_busy_<workload>.txt from a rocprofv3 --pmc "
+                         "--kernel-trace run and the bench line it printed, and exit")
+    ap.add_argument("--summarize-sweep", nargs="+", metavar="BENCH_LOG",
+                    help="write profiles/sweep_sq_lvx_2k_128k.txt from bench lines at several "
+                         "S_Q and exit")
     ap.add_argument("--summarize-rounds", nargs=2, metavar=("CONTIGUOUS_DIR", "STRIPED_DIR"),
                     help="write profiles/rounds_<workload>.txt from two rocprofv3 kernel traces "
                          "of ROUNDS mode (causal rows in sequence order, then striped) and exit")
     ap.add_argument("--profiled-command", default="python3 bench.py",
                     help="the command line the summarized profiler runs used")
     args = ap.parse_args()
+    mode = args.mode or DEFAULT_MODE.get(args.workload, "split")
+    name = args.workload + ("_weight_grads" if args.weight_grads else "") + \
+        ("_striped" if args.striped else "")
     if args.summarize_traffic:
-        print(summarize_traffic(*args.summarize_traffic, args.mode, args.profiled_command))
+        print(summarize_traffic(*args.summarize_traffic, args.workload, mode,
+                                args.profiled_command))
         return
     if args.summarize_rounds:
         from ring_exact_attention_amd.inputs import WORKLOADS
@@ -209,8 +400,13 @@ def main():
                                WORKLOADS[args.workload].n, args.profiled_command))
         return
     if args.summarize_stats:
-        name = args.workload + ("_weight_grads" if args.weight_grads else "")
-        print(summarize_stats(args.summarize_stats, name, args.profiled_command))
+        print(summarize_stats(*args.summarize_stats, name, args.profiled_command))
+        return
+    if args.summarize_counters:
+        print(summarize_counters(*args.summarize_counters, name, args.profiled_command))
+        return
+    if args.summarize_sweep:
+        print(summarize_sweep(args.summarize_sweep, args.profiled_command))
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -230,6 +426,8 @@ def main():
         hip_build.build()
     bwa.lib()
     w = WORKLOADS[args.workload]
+    if args.sq:
+        w = w.resized(SQ=args.sq, SKV=w.SKV if not w.causal else args.sq)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     recompute = w.E > 0
@@ -242,7 +440,7 @@ def main():
         v = torch.empty_like(k)
         bwa.bwa_kv_recompute(y, wk, wv, w.H, w.D, k=k, v=v)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        bmode = "rounds" if args.mode in ("rounds", "rounds_transfer") else "fused"
+        bmode = "rounds" if mode in ("rounds", "rounds_transfer") else "fused"
         bws = torch.empty(max(bwa.ring_bwd_workspace(q, k, w.n, bmode), 1), dtype=torch.uint8,
                           device=dev)
         if args.weight_grads:
@@ -253,13 +451,13 @@ def main():
         q, k, v = make_qkv(w, device=dev)
     o = torch.empty_like(q)
     lse = torch.empty(w.B, w.H, w.SQ, dtype=torch.float32, device=dev)
-    nbytes = bwa.ring_fwd_workspace(q, k, w.n, args.mode)
+    nbytes = bwa.ring_fwd_workspace(q, k, w.n, mode)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    causal = "striped" if args.striped and w.causal else w.causal
 
     def fwd():
-        bwa.bwa_ring_fwd(q, k, v, w.n, args.sched, args.mode,
-                         causal=("striped" if args.striped and w.causal else w.causal),
-                         scale=w.scale, o=o, lse=lse, workspace=ws)
+        bwa.bwa_ring_fwd(q, k, v, w.n, args.sched, mode, causal=causal, scale=w.scale, o=o,
+                         lse=lse, workspace=ws)
 
     def step():
         if recompute:
@@ -268,7 +466,7 @@ def main():
             bwa.bwa_kv_recompute(y, wk, wv, w.H, w.D, k=k, v=v)
             fwd()
             bwa.bwa_kv_recompute(y, wk, wv, w.H, w.D, k=k, v=v)
-            bwa.bwa_ring_bwd(q, k, v, o, lse, do, w.n, args.sched, bmode, causal=w.causal,
+            bwa.bwa_ring_bwd(q, k, v, o, lse, do, w.n, args.sched, bmode, causal=causal,
                              scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=bws)
             if args.weight_grads:
                 bwa.bwa_kv_recompute_bwd(y, wk, wv, dk, dv, dwk_t=dwk, dwv_t=dwv, dy=dyf)
@@ -288,8 +486,11 @@ def main():
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
-    ms = sum(per_step_ms) / len(per_step_ms)
+    per_step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    mid = len(per_step_ms) // 2
+    ms = (per_step_ms[mid] if len(per_step_ms) % 2 else
+          0.5 * (per_step_ms[mid - 1] + per_step_ms[mid]))
+    ms_mean = sum(per_step_ms) / len(per_step_ms)
 
     if w.causal:
         flops = 4.0 * w.B * w.H * w.D * w.SQ * (w.SQ + 1) / 2
@@ -307,9 +508,9 @@ def main():
 
     # Dominant kernel: in fused mode the step is one launch of the block-pair
     # kernel; in rounds mode n launches (one per round) plus a small finalize;
-    # in split mode one launch plus the merge.  Per-launch flops are the
-    # step's flops divided by the launches of that kernel.
-    launches = w.n if args.mode in ("rounds", "rounds_transfer") else 1
+    # in split mode one launch plus the merge.  Per-launch work is the step's
+    # work divided by the launches of that kernel.
+    launches = w.n if mode in ("rounds", "rounds_transfer") else 1
     if recompute:
         # several kernels per step (GEMM, forward, backward); report the step as a whole
         roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
@@ -322,7 +523,8 @@ def main():
         # the forward kernel's share of the step: in split mode the merge kernel is
         # the rest; its duration is measured separately below
         fwd_ms = ms
-        if args.mode == "split":
+        part_bytes = 0
+        if mode == "split":
             # the step is two launches: every pair's partial, then the ordered
             # merge; time the merge alone on the same workspace and subtract
             from ring_exact_attention_amd._bwa import split_workspace_views
@@ -336,27 +538,44 @@ def main():
             torch.cuda.synchronize()
             merge = em[0].elapsed_time(em[1]) / args.steps
             fwd_ms = max(ms - merge, 1e-6)
-        achieved = (flops / launches) / ((fwd_ms * 1e-3) / launches) / 1e12
-        traffic = read_traffic(args.mode) if args.workload == "lvx_2k_128k" else None
-        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                    "traffic": traffic, "kernel": "fwd_bf16_kernel<128>",
-                    "launches_per_step": launches,
-                    "kernel_ms_per_launch": round(fwd_ms / launches, 4),
-                    "other_ms_per_step": round(ms - fwd_ms, 4)}
+            part_bytes = w.n * w.B * w.H * w.SQ * (w.D + 1) * 4  # partials written
+        kernel_ms = fwd_ms / launches
+        traffic = read_traffic(args.workload, mode) if not args.sq else None
+        busy, clock = read_counters(args.workload, mode) if not args.sq else (None, None)
+        if args.workload in HBM_BOUND:
+            # algorithmic bytes of one pair-kernel launch: Q, K, V read once, the
+            # partials (split) or the output and LSE written
+            alg = (w.B * w.H * (w.SQ + 2 * w.SKV) * w.D * esz +
+                   (part_bytes if part_bytes else w.B * w.H * w.SQ * (w.D * esz + 4)))
+            achieved = alg / launches / (kernel_ms * 1e-3) / 1e9
+            roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                        "traffic": traffic, "algorithmic_bytes_per_launch": alg // launches,
+                        "mfma_frac": round(flops / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        else:
+            achieved = (flops / launches) / (kernel_ms * 1e-3) / 1e12
+            roofline = {"bound": "mfma", "achieved": round(achieved, 2),
+                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+        roofline.update({"kernel": "fwd_bf16_kernel<128>", "launches_per_step": launches,
+                         "kernel_ms_per_launch": round(kernel_ms, 4),
+                         "other_ms_per_step": round(ms - fwd_ms, 4),
+                         "mfma_busy_profiled": busy, "clock_ghz_profiled": clock})
 
     out = {
-        "metric": METRIC if args.workload == "lvx_2k_128k" else
+        "metric": METRIC if (args.workload == "lvx_2k_128k" and not args.sq) else
         f"{'training-step' if recompute else 'attention'} TFLOP/s, {w.name}"
-        f"{' with weight gradients' if args.weight_grads else ''}, 1 GPU",
+        f"{' with weight gradients' if args.weight_grads else ''}"
+        f"{f' at S_Q={w.SQ}' if args.sq else ''}, 1 GPU",
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
-        "ms_per_step_min": round(min(per_step_ms), 4),
-        "ms_per_step_max": round(max(per_step_ms), 4),
+        "ms_per_step_min": round(per_step_ms[0], 4),
+        "ms_per_step_max": round(per_step_ms[-1], 4),
+        "ms_per_step_mean": round(ms_mean, 4),
         "wall_s_timed": round(wall, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -365,8 +584,7 @@ def main():
         "data": "synthetic",
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "S_Q": w.SQ, "S_KV": w.SKV, "D": w.D,
-                   "n_shards": w.n, "schedule": args.sched, "mode": args.mode,
-                   "causal": ("striped" if args.striped and w.causal else w.causal),
+                   "n_shards": w.n, "schedule": args.sched, "mode": mode, "causal": causal,
                    "seed": w.seed},
         "roofline": roofline,
     }
@@ -380,7 +598,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    if not args.no_cpu_baseline and not recompute:
+    if not args.no_cpu_baseline and not recompute and not args.sq:
         out["cpu_baseline"] = cpu_baseline(q, k, v, w, args.cpu_rows_per_head)
     else:
         out["cpu_baseline"] = None
