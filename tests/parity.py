@@ -28,6 +28,14 @@ Gradients (bf16 outputs, fp32 accumulation), element by element:
   the chi spread of a 128-element row, 6e-3 < 1.5e-2; the floor covers rows
   whose exact gradient vanishes (causal row 0 of dQ, where dP and Delta are
   the same fp32 sum in two orders).
+  dQ rows add one more term (dq_row_allowance): Delta = rowsum(dO * O) is
+  formed from the forward's bf16 output, whose elements carry about two
+  roundings, so Delta_i is off by dDelta_i ~ N(0, sigma_i^2), sigma_i =
+  u sqrt(2/3) ||dO_i * O_i||, and dS_ij = P_ij (dP_ij - Delta_i) moves
+  dQ_i by -scale dDelta_i sum_j P_ij K_j.  That is negligible against a long
+  row's gradient, but a causal row with few keys whose exact gradient nearly
+  cancels (dP_ij close to Delta_i for all its keys) sees it whole: its bound
+  gets 6 scale sigma_i ||sum_j P_ij K_j||.
 """
 from __future__ import annotations
 
@@ -79,7 +87,18 @@ def check_fwd(o, lse, o_ref, lse_ref, dtype, what=""):
     return float(err.max())
 
 
-def check_grad(g, g_ref, what="", block=128):
+def dq_row_allowance(orc, q, k, v, do, scale, causal):
+    """Per-row allowance [B*H, S_Q] for dQ from the rounding of Delta (module
+    docstring): 6 scale sigma_i ||sum_j P_ij K_j|| with sigma_i = u sqrt(2/3)
+    ||dO_i * O_i||; O and sum_j P_ij K_j (attention with V = K) from the oracle."""
+    B, H, SQ, D = q.shape
+    O, _ = orc.attn_fwd(q, k, v, scale, causal=causal)
+    PK, _ = orc.attn_fwd(q, k, k, scale, causal=causal)
+    sigma = U_BF16 * np.sqrt(2.0 / 3.0) * np.linalg.norm(to64(do) * O, axis=-1)
+    return (6.0 * scale * sigma * np.linalg.norm(PK, axis=-1)).reshape(B * H, SQ)
+
+
+def check_grad(g, g_ref, what="", block=128, row_extra=None):
     """Element-wise gradient check (bounds in the module docstring).  g and
     g_ref are [..., rows, D]; blocks are `block` consecutive rows of one
     leading index (one head).  Prints and returns the error summary,
@@ -107,7 +126,8 @@ def check_grad(g, g_ref, what="", block=128):
     rn = np.linalg.norm(r3, axis=-1)
     en = np.linalg.norm(g3 - r3, axis=-1)
     rms_row = np.sqrt((rn ** 2).mean())
-    row_ratio = en / (GRAD_ROW * rn + GRAD_ROW_FLOOR * rms_row + 1e-300)
+    extra = 0.0 if row_extra is None else np.asarray(row_extra, np.float64).reshape(rn.shape)
+    row_ratio = en / (GRAD_ROW * rn + GRAD_ROW_FLOOR * rms_row + extra + 1e-300)
     print(f"grad {what}: max_rel {max_rel:.3e} block_max {worst_block:.3e} "
           f"mean {mean_ratio:.3e} fro {fro:.3e} row {row_ratio.max() * GRAD_ROW:.3e}", flush=True)
     assert worst_block <= GRAD_BLOCK_MAX, f"{what}: block max err {worst_block:.3e} of block max"
