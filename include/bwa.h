@@ -54,8 +54,10 @@
  *     Every round is a perfect matching and the n rounds cover all n^2
  *     pairs.  Query block j therefore merges KV shards in the order
  *     j, j+1, ... (KV-stationary) or j, j-1, ... (Q-stationary), mod n.
- *   - Thread safety: no mutable global state; calls on different streams
- *     may run concurrently if their output buffers are disjoint.
+ *   - Thread safety: calls on different streams may run concurrently if
+ *     their output buffers are disjoint.  The only mutable global state is
+ *     the per-device address of the scratch array of
+ *     bwa_ring_bwd_noalloc, looked up once under a lock.
  */
 #ifndef BWA_H_
 #define BWA_H_
@@ -215,6 +217,29 @@ bwa_status bwa_ring_bwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tens
                         bwa_schedule sched, bwa_mode mode, int causal, float scale,
                         const bwa_tensor* dq, const bwa_tensor* dk, const bwa_tensor* dv,
                         void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * bwa_ring_bwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and arguments without a workspace.  Its scratch
+ * (Delta, fp32 [B, H, S_Q]) lives in a library-owned device array of
+ * BWA_NOALLOC_SCRATCH_BYTES per GPU, which each GPU the library runs on holds
+ * until the process ends.  Nothing is allocated or freed by the call.
+ *   - mode FUSED or SPLIT (the same for the backward); ROUNDS gives
+ *     BWA_ERR_UNSUPPORTED (its fp32 accumulators do not fit the array).
+ *   - B * H * S_Q * 4 bytes (rounded up to 256) above the array's size give
+ *     BWA_ERR_WORKSPACE: at most 4,194,304 query rows over all heads.
+ *   - Every call on one GPU uses that GPU's one array, and Delta is rewritten
+ *     in full by each call before it is read: calls that overlap on one GPU
+ *     (different streams without ordering) race.
+ * Results are bitwise those of bwa_ring_bwd in FUSED mode.
+ */
+#define BWA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+bwa_status bwa_ring_bwd_noalloc(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v,
+                                const bwa_tensor* o, const float* lse, const bwa_tensor* dout,
+                                int n, bwa_schedule sched, bwa_mode mode, int causal, float scale,
+                                const bwa_tensor* dq, const bwa_tensor* dk, const bwa_tensor* dv,
+                                void* stream);
 
 /*
  * Recompute of keys and values from the one shared copy of the visual

@@ -18,6 +18,7 @@ from ._bwa import (  # noqa: F401
     bwa_merge_partials,
     bwa_partial_fwd,
     bwa_ring_bwd,
+    bwa_ring_bwd_noalloc,
     bwa_ring_fwd,
     lib,
     ring_bwd_workspace,
@@ -25,5 +26,5 @@ from ._bwa import (  # noqa: F401
 )
 
 __all__ = ["bwa_partial_fwd", "bwa_merge", "bwa_merge_partials", "bwa_ring_fwd", "bwa_ring_bwd",
-           "bwa_kv_recompute", "bwa_kv_recompute_bwd", "bwa_choose_schedule",
+           "bwa_ring_bwd_noalloc", "bwa_kv_recompute", "bwa_kv_recompute_bwd", "bwa_choose_schedule",
            "BwaError", "lib"]

@@ -29,7 +29,8 @@ MODES = {"rounds": MODE_ROUNDS, "fused": MODE_FUSED, "split": MODE_SPLIT,
 
 EXPORTED = ("bwa_partial_fwd", "bwa_merge", "bwa_merge_partials", "bwa_ring_fwd_workspace",
             "bwa_ring_fwd",
-            "bwa_ring_bwd_workspace", "bwa_ring_bwd", "bwa_kv_recompute", "bwa_kv_recompute_bwd",
+            "bwa_ring_bwd_workspace", "bwa_ring_bwd", "bwa_ring_bwd_noalloc", "bwa_kv_recompute",
+            "bwa_kv_recompute_bwd",
             "bwa_choose_schedule",
             "bwa_status_string",
             "bwa_last_error", "bwa_version")
@@ -78,10 +79,11 @@ def lib():
         L.bwa_ring_bwd_workspace.argtypes = [T, T, ci, ci]
         L.bwa_ring_bwd_workspace.restype = sz
         L.bwa_ring_bwd.argtypes = [T, T, T, T, vp, T, ci, ci, ci, ci, f32, T, T, T, vp, sz, vp]
+        L.bwa_ring_bwd_noalloc.argtypes = [T, T, T, T, vp, T, ci, ci, ci, ci, f32, T, T, T, vp]
         L.bwa_kv_recompute.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int32, T, T,
                                        vp]
         for name in ("bwa_partial_fwd", "bwa_merge", "bwa_merge_partials", "bwa_ring_fwd",
-                     "bwa_ring_bwd", "bwa_kv_recompute"):
+                     "bwa_ring_bwd", "bwa_ring_bwd_noalloc", "bwa_kv_recompute"):
             getattr(L, name).restype = ci
         L.bwa_kv_recompute_bwd.argtypes = [vp, vp, vp, T, T, i64, i64, i64, i64, i64, vp, vp, vp,
                                            ctypes.c_int32, vp]
@@ -284,6 +286,22 @@ def bwa_ring_bwd(q, k, v, o, lse, dout, n, sched="kv", mode="fused", causal=Fals
                               _sched(sched), m, _causal(causal), float(scale),
                               ctypes.byref(t[5]), ctypes.byref(t[6]), ctypes.byref(t[7]),
                               _ptr(ws), nbytes, _stream(q.device)))
+    return dq, dk, dv
+
+
+def bwa_ring_bwd_noalloc(q, k, v, o, lse, dout, n, dq, dk, dv, sched="kv", mode="fused",
+                         causal=False, scale=None):
+    """bwa_ring_bwd with the library's static scratch array instead of a
+    workspace: the caller passes every output; nothing is allocated."""
+    D = q.shape[-1]
+    scale = D ** -0.5 if scale is None else scale
+    _need_f32("lse", lse, q.shape[0] * q.shape[1] * q.shape[2])
+    t = [as_bwa(x) for x in (q, k, v, o, dout, dq, dk, dv)]
+    _check(lib().bwa_ring_bwd_noalloc(ctypes.byref(t[0]), ctypes.byref(t[1]), ctypes.byref(t[2]),
+                                      ctypes.byref(t[3]), _ptr(lse), ctypes.byref(t[4]), int(n),
+                                      _sched(sched), _mode(mode), _causal(causal), float(scale),
+                                      ctypes.byref(t[5]), ctypes.byref(t[6]), ctypes.byref(t[7]),
+                                      _stream(q.device)))
     return dq, dk, dv
 
 

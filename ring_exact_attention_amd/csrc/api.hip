@@ -26,6 +26,8 @@ hipError_t gemm_grad_launch(const void* y, const void* wk_t, const void* wv_t,
                             const bwa_tensor* dk, const bwa_tensor* dv, int64_t B, int64_t S,
                             int64_t E, int64_t H, int64_t Dh, float* dwk_t, float* dwv_t,
                             float* dy, int accumulate, hipStream_t st);
+size_t scratch_bytes();
+hipError_t scratch_ptr(void** out);
 hipError_t gemm_kv_launch(const void* y, const void* wk_t, const void* wv_t, int64_t B, int64_t S,
                           int64_t E, int64_t H, int64_t D, const bwa_tensor* k,
                           const bwa_tensor* v, hipStream_t st);
@@ -436,11 +438,15 @@ size_t bwa_ring_bwd_workspace(const bwa_tensor* q, const bwa_tensor* k, int n, b
   return bwa::bwd_workspace_bytes(q->B * q->H, q->S, k->S, (int)q->D, n, mode);
 }
 
-bwa_status bwa_ring_bwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v,
-                        const bwa_tensor* o, const float* lse, const bwa_tensor* dout, int n,
-                        bwa_schedule sched, bwa_mode mode, int causal, float scale,
-                        const bwa_tensor* dq, const bwa_tensor* dk, const bwa_tensor* dv,
-                        void* workspace, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by bwa_ring_bwd and its allocation-free variant.
+bwa_status check_bwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v,
+                     const bwa_tensor* o, const float* lse, const bwa_tensor* dout, int n,
+                     bwa_schedule sched, bwa_mode mode, int causal, float scale,
+                     const bwa_tensor* dq, const bwa_tensor* dk, const bwa_tensor* dv) {
   bwa_status s;
   if ((s = check_qkv(q, k, v, causal)) != BWA_OK) return s;
   if ((s = check_like(o, q, q->S, "o")) != BWA_OK) return s;
@@ -457,16 +463,15 @@ bwa_status bwa_ring_bwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tens
     return fail(BWA_ERR_UNSUPPORTED, "striped causal order needs n to divide S");
   if (!bwa::bwd_supported(q->dtype, (int)q->D))
     return fail(BWA_ERR_UNSUPPORTED, "backward implemented for bf16 only (D = 64 or 128)");
-  if (q->S == 0) return BWA_OK;
-  if (!lse) return fail(BWA_ERR_INVALID_ARG, "lse is NULL");
-  const int64_t BH = q->B * q->H;
-  size_t need = bwa::bwd_workspace_bytes(BH, q->S, k->S, (int)q->D, n, mode);
-  if (need > 0) {
-    if (!workspace || ws_bytes < need)
-      return fail(BWA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
-    if ((uintptr_t)workspace % 256 != 0)
-      return fail(BWA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  }
+  if (q->S > 0 && !lse) return fail(BWA_ERR_INVALID_ARG, "lse is NULL");
+  return BWA_OK;
+}
+
+bwa_status run_bwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v,
+                   const bwa_tensor* o, const float* lse, const bwa_tensor* dout, int n,
+                   bwa_schedule sched, bwa_mode mode, int causal, float scale,
+                   const bwa_tensor* dq, const bwa_tensor* dk, const bwa_tensor* dv,
+                   void* workspace, void* stream) {
   bwa::BwdArgs a = {};
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
   a.lse = lse;
@@ -479,6 +484,55 @@ bwa_status bwa_ring_bwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tens
   hipError_t e = bwa::bwd_run(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "ring backward launch");
   return BWA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bwa_status bwa_ring_bwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v,
+                        const bwa_tensor* o, const float* lse, const bwa_tensor* dout, int n,
+                        bwa_schedule sched, bwa_mode mode, int causal, float scale,
+                        const bwa_tensor* dq, const bwa_tensor* dk, const bwa_tensor* dv,
+                        void* workspace, size_t ws_bytes, void* stream) {
+  bwa_status s = check_bwd(q, k, v, o, lse, dout, n, sched, mode, causal, scale, dq, dk, dv);
+  if (s != BWA_OK) return s;
+  if (q->S == 0) return BWA_OK;
+  const int64_t BH = q->B * q->H;
+  size_t need = bwa::bwd_workspace_bytes(BH, q->S, k->S, (int)q->D, n, mode);
+  if (need > 0) {
+    if (!workspace || ws_bytes < need)
+      return fail(BWA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    if ((uintptr_t)workspace % 256 != 0)
+      return fail(BWA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  return run_bwd(q, k, v, o, lse, dout, n, sched, mode, causal, scale, dq, dk, dv, workspace,
+                 stream);
+}
+
+bwa_status bwa_ring_bwd_noalloc(const bwa_tensor* q, const bwa_tensor* k, const bwa_tensor* v,
+                                const bwa_tensor* o, const float* lse, const bwa_tensor* dout,
+                                int n, bwa_schedule sched, bwa_mode mode, int causal, float scale,
+                                const bwa_tensor* dq, const bwa_tensor* dk, const bwa_tensor* dv,
+                                void* stream) {
+  bwa_status s = check_bwd(q, k, v, o, lse, dout, n, sched, mode, causal, scale, dq, dk, dv);
+  if (s != BWA_OK) return s;
+  if (mode == BWA_MODE_ROUNDS)
+    return fail(BWA_ERR_UNSUPPORTED,
+                "the allocation-free backward runs FUSED (or SPLIT, the same); ROUNDS carries "
+                "fp32 dQ/dK/dV accumulators beyond its scratch array");
+  if (q->S == 0) return BWA_OK;
+  const size_t need =
+      bwa::bwd_workspace_bytes(q->B * q->H, q->S, k->S, (int)q->D, n, BWA_MODE_FUSED);
+  if (need > bwa::scratch_bytes())
+    return fail(BWA_ERR_WORKSPACE,
+                "scratch of %zu bytes needed (B*H*S_Q*4), the allocation-free backward has %zu",
+                need, bwa::scratch_bytes());
+  void* ptr = nullptr;
+  hipError_t e = bwa::scratch_ptr(&ptr);
+  if (e != hipSuccess) return hip_fail(e, "scratch array address");
+  return run_bwd(q, k, v, o, lse, dout, n, sched, BWA_MODE_FUSED, causal, scale, dq, dk, dv, ptr,
+                 stream);
 }
 
 bwa_status bwa_kv_recompute(const void* y, const void* wk_t, const void* wv_t, int64_t B,

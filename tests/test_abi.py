@@ -278,3 +278,20 @@ def test_binding_rejects_missized_buffers():
         _bwa.bwa_merge(a, la, a, la, o_out=a.bfloat16(), lse_out=f(16))
     with pytest.raises(ValueError, match="lse_out has"):
         _bwa.bwa_merge(a, la, a, la, o_out=f(16, 64), lse_out=f(17))
+
+
+def test_ring_bwd_noalloc_validation(L):
+    """Host-side checks of the allocation-free backward, before any device call."""
+    def call(S, mode=1, H=2):
+        t = T(H=H, S=S)
+        return L.bwa_ring_bwd_noalloc(*[ctypes.byref(t)] * 4, FAKE, ctypes.byref(t), 4, 0, mode,
+                                      0, 0.1, *[ctypes.byref(t)] * 3, None)
+    expect(L, call(64, mode=_bwa.MODE_ROUNDS), _bwa.BWA_ERR_UNSUPPORTED, "ROUNDS")
+    expect(L, call(64, mode=_bwa.MODE_ROUNDS_TRANSFER), _bwa.BWA_ERR_UNSUPPORTED, "forward mode")
+    # 128 heads x 32769 rows x 4 bytes of Delta exceed the 16 MiB array
+    expect(L, call(32769, H=128), _bwa.BWA_ERR_WORKSPACE, "scratch")
+    q0, kk = T(S=0), T(S=64)  # empty query: nothing to do, nothing touched
+    assert L.bwa_ring_bwd_noalloc(ctypes.byref(q0), ctypes.byref(kk), ctypes.byref(kk),
+                                  ctypes.byref(q0), None, ctypes.byref(q0), 4, 0, 1, 0, 0.1,
+                                  ctypes.byref(q0), ctypes.byref(kk), ctypes.byref(kk),
+                                  None) == _bwa.BWA_OK
