@@ -203,7 +203,10 @@ size_t bwa_ring_bwd_workspace(const bwa_tensor* q, const bwa_tensor* k, int n, b
  * Each block pair contributes additively, using the global LSE and Delta.
  * KV-stationary: dK, dV stay with their shard while (Q, dO, LSE, Delta, dQ)
  * rotate; Q-stationary: the reverse.  Modes as in bwa_ring_fwd (SPLIT is
- * treated as FUSED).
+ * treated as FUSED): ROUNDS runs the rounds as launches in the schedule's
+ * order; FUSED accumulates dQ over the KV shards in the schedule's order and,
+ * for rows in sequence order (causal 0 or 1), dK and dV over all query rows
+ * in sequence order (the same sums; only fp32 rounding differs).
  *   o, dout [B, H, S_Q, D] and lse fp32 [B, H, S_Q] from the forward.
  *   dq [B, H, S_Q, D], dk and dv [B, H, S_KV, D] in q's dtype (overwritten).
  *   causal: 0, 1 or 2 as in the conventions above (the forward's value).

@@ -33,6 +33,9 @@ struct BwdParams {
   float* dk_acc;  // ROUNDS: [BH][SKV][D]
   float* dv_acc;  // ROUNDS: [BH][SKV][D]
   int B, H, SQ, SKV, n, sched, mode, causal, round;
+  int nq;  // dK/dV kernel: query blocks it walks (n, or 1 for the whole range)
+  int nk;  // dQ kernel: key shards it walks (n, or 1 for the whole range)
+  int kv_tiles;  // dK/dV kernel: key tiles per shard if the grid is head-major, else 0
   int tiles, groups;
   float scale, scale_log2;
 };
@@ -58,7 +61,7 @@ __device__ inline bf16x8 pack8(const f32x16& c, int h) {
 //   Q-stationary kernel: a query tile of block j meets shards (j + r) mod n or
 //     (j - r) mod n, the same order as the forward merge.
 __device__ inline int qblock_at_step(int sched, int n, int s, int r) {
-  return sched == SCHED_KV_STATIONARY ? ((s - r) % n + n) % n : (s + r) % n;
+  return sched == SCHED_KV_STATIONARY ? ring_sub(s, r, n) : ring_add(s, r, n);
 }
 
 }  // namespace
@@ -176,7 +179,16 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
   int g_, t_;
   if (!xcd_group_tile(blockIdx.x, p.tiles, p.groups, &g_, &t_)) return;
   const int BH = p.B * p.H;
-  const int bh = g_ % BH;
+  // group = (shard or round worker, head), tile = key tile of that shard;
+  // or, head-major (FUSED with at least 8 heads): group = head and tile =
+  // (shard, key tile), so that all of a head's key tiles run back to back on
+  // one XCD and share its Q and dO in that XCD's L2.
+  const bool head_major = p.kv_tiles > 0;
+  const int bh = head_major ? g_ : g_ % BH;
+  if (head_major) {
+    g_ = (t_ / p.kv_tiles) * BH + bh;  // the (shard, head) group index
+    t_ = t_ % p.kv_tiles;
+  }
   int shard, nseg, fixed_qb = -1;
   bool acc_in = false;
   if (p.mode == MODE_ROUNDS) {
@@ -186,9 +198,15 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
     nseg = 1;
     acc_in = p.round > 0;
   } else {
+    // FUSED walks p.nq query blocks: n in the schedule's order, or (rows in
+    // sequence order) 1, all query rows as one segment; dK and dV are sums
+    // over the query rows, the same in any block order up to fp32 rounding,
+    // and a switch of segment costs about one query step.  The striped order
+    // keeps one segment per query shard (its mask shift changes per shard).
     shard = g_ / BH;
-    nseg = p.n;
+    nseg = p.nq;
   }
+  const int qs0 = p.nq == 1 ? 0 : shard;  // the query block walked first
   const int64_t ks = shard_start(p.SKV, p.n, shard), ke = shard_start(p.SKV, p.n, shard + 1);
   const int64_t kt0 = ks + (int64_t)t_ * BK;
   const int64_t kt1 = min(ke, kt0 + BK);
@@ -222,8 +240,8 @@ __global__ __launch_bounds__(64 * kDkdvWaves) void bwd_dkdv_kernel(BwdParams p) 
   };
   auto seek = [&](It& it, int from) {
     for (it.r = from; it.r < nseg; ++it.r) {
-      int qb = fixed_qb >= 0 ? fixed_qb : qblock_at_step(p.sched, p.n, shard, it.r);
-      int64_t a = shard_start(p.SQ, p.n, qb), e = shard_start(p.SQ, p.n, qb + 1);
+      int qb = fixed_qb >= 0 ? fixed_qb : qblock_at_step(p.sched, p.nq, qs0, it.r);
+      int64_t a = shard_start(p.SQ, p.nq, qb), e = shard_start(p.SQ, p.nq, qb + 1);
       it.qo = CM == 2 ? (int)(a - ks) + (shard > qb ? 1 : 0) : 0;
       if (CAUSAL && a < kt0 + it.qo) a = kt0 + it.qo;  // rows before that see none of the tile
       if (e > a) {
@@ -551,9 +569,14 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdParams p) {
     nseg = 1;
     acc_in = p.round > 0;
   } else {
+    // FUSED walks p.nk key segments: the n shards in the schedule's order, or
+    // (rows in sequence order) 1, all keys in sequence order, so that the
+    // query tiles of a head stream the same K, V tiles at the same time; dQ
+    // is a sum over the keys, the same in any order up to fp32 rounding.
     j = p.causal ? (p.n - 1 - g_ / BH) : (g_ / BH);
-    nseg = p.n;
+    nseg = p.nk;
   }
+  const int ks0 = p.nk == 1 ? 0 : j;  // the key segment walked first
   const int64_t qs = shard_start(p.SQ, p.n, j), qe = shard_start(p.SQ, p.n, j + 1);
   const int64_t r0 = qs + (int64_t)t_ * BM;
   const int64_t r1 = min(qe, r0 + BM);
@@ -598,8 +621,8 @@ __global__ __launch_bounds__(64 * kDqWaves) void bwd_dq_kernel(BwdParams p) {
   };
   auto seek = [&](It& it, int from) {
     for (it.r = from; it.r < nseg; ++it.r) {
-      int kb = fixed_kb >= 0 ? fixed_kb : shard_at_step(p.sched, p.n, j, it.r);
-      int64_t a = shard_start(p.SKV, p.n, kb), e = shard_start(p.SKV, p.n, kb + 1);
+      int kb = fixed_kb >= 0 ? fixed_kb : shard_at_step(p.sched, p.nk, ks0, it.r);
+      int64_t a = shard_start(p.SKV, p.nk, kb), e = shard_start(p.SKV, p.nk, kb + 1);
       it.ko = CM == 2 ? (int)(a - qs) - (kb > j ? 1 : 0) : 0;
       if (CAUSAL && e > r1 + it.ko) e = r1 + it.ko;  // keys after the job's last row's last key
       if (e > a) {
@@ -883,14 +906,19 @@ static hipError_t bwd_launch_all(BwdParams p, hipStream_t st) {
   const int q_tiles = (int)(((p.SQ + p.n - 1) / p.n + BM - 1) / BM);
   const int groups = (int)(BH * p.n);
   const int rounds = p.mode == MODE_ROUNDS ? p.n : 1;
+  // FUSED dK/dV with at least one head per XCD: head-major grid
+  const bool head_major = p.mode != MODE_ROUNDS && BH >= kNumXcd;
   for (int r = 0; r < rounds; ++r) {
     p.round = r;
-    p.groups = groups;
-    p.tiles = kv_tiles;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CM>), dim3(xcd_grid_size(kv_tiles, groups)),
+    p.kv_tiles = head_major ? kv_tiles : 0;
+    p.groups = head_major ? (int)BH : groups;
+    p.tiles = head_major ? kv_tiles * p.n : kv_tiles;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CM>), dim3(xcd_grid_size(p.tiles, p.groups)),
                        dim3(64 * kDkdvWaves), 0, st, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     p.tiles = q_tiles;
+    p.groups = groups;
+    p.kv_tiles = 0;
     hipLaunchKernelGGL((bwd_dq_kernel<D, CM>), dim3(xcd_grid_size(q_tiles, groups)),
                        dim3(64 * kDqWaves), 0, st, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -942,6 +970,8 @@ hipError_t bwd_run(const BwdArgs& a, hipStream_t st) {
   p.sched = a.sched;
   p.mode = a.mode == MODE_ROUNDS ? MODE_ROUNDS : MODE_FUSED;
   p.causal = a.causal;
+  p.nq = (p.mode == MODE_ROUNDS || p.causal == 2) ? p.n : 1;
+  p.nk = p.nq;
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
   const int Dh = (int)a.q->D;

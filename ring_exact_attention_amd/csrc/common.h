@@ -40,20 +40,26 @@ __host__ __device__ inline int64_t shard_start(int64_t S, int n, int k) {
   return (int64_t)k * S / n;
 }
 
-// Pair held by virtual worker w in round r.
+// (a - b) mod n and (a + b) mod n for 0 <= a, b < n, without a division.
+__host__ __device__ inline int ring_sub(int a, int b, int n) { return a >= b ? a - b : a - b + n; }
+__host__ __device__ inline int ring_add(int a, int b, int n) { return a + b < n ? a + b : a + b - n; }
+
+// Pair held by virtual worker w in round r (0 <= w, r < n).
 //   KV-stationary: Q block (w - r) mod n with KV shard w.
 //   Q-stationary:  Q block w with KV shard (w - r) mod n.
 __host__ __device__ inline void ring_pair(int sched, int n, int r, int w, int* qb, int* kb) {
-  int moved = ((w - r) % n + n) % n;
+  int moved = ring_sub(w, r, n);
   if (sched == SCHED_KV_STATIONARY) { *qb = moved; *kb = w; }
   else { *qb = w; *kb = moved; }
 }
 
-// KV shard merged into query block j at step r of its schedule order:
-// KV-stationary visits j, j+1, ...; Q-stationary visits j, j-1, ... (mod n).
+// KV shard merged into query block j at step r of its schedule order
+// (0 <= j, r < n): KV-stationary visits j, j+1, ...; Q-stationary visits
+// j, j-1, ... (mod n).
 __host__ __device__ inline int shard_at_step(int sched, int n, int j, int r) {
-  return sched == SCHED_KV_STATIONARY ? (j + r) % n : ((j - r) % n + n) % n;
+  return sched == SCHED_KV_STATIONARY ? ring_add(j, r, n) : ring_sub(j, r, n);
 }
+
 
 // Forward launch description (one struct for every mode and dtype).
 struct FwdParams {

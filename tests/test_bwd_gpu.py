@@ -50,6 +50,10 @@ BWD_SHAPES = [
     (1, 1, 300, 300, 5, "striped", 128),  # shards of 60: ragged tiles inside each shard
     (2, 1, 1024, 1024, 8, "striped", 128),
     (1, 2, 384, 384, 3, "striped", 64),
+    # at least 8 heads: the fused dK/dV grid is laid out head by head
+    (2, 4, 300, 1000, 4, False, 128),
+    (1, 8, 384, 384, 3, True, 64),
+    (1, 8, 256, 256, 2, "striped", 128),
 ]
 
 
