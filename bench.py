@@ -324,6 +324,66 @@ def summarize_rounds(trace_dirs, labels, workload: str, n: int, command: str) ->
     return text
 
 
+def summarize_pmc(pmc_dir: str, bench_log: str, name: str, tag: str, command: str) -> str:
+    """Write profiles/<tag>_<name>.txt: every counter of a rocprofv3 --pmc run
+    with --kernel-trace, per kernel, averaged over the timed steps' dispatches
+    (values as rocprofv3 reports them per dispatch, summed over its instances)."""
+    import collections
+    import csv
+    b = _bench_line(bench_log)
+    steps, warm = b["steps"], b["warmup"]
+    vals = collections.defaultdict(lambda: collections.defaultdict(float))
+    names = {}
+    for r in csv.DictReader(open(_find(pmc_dir, "counter_collection.csv"))):
+        d = int(r["Dispatch_Id"])
+        vals[d][r["Counter_Name"]] += float(r["Counter_Value"])
+        names[d] = r["Kernel_Name"]
+    starts, durs = {}, {}
+    for r in csv.DictReader(open(_find(pmc_dir, "kernel_trace.csv"))):
+        d = int(r["Dispatch_Id"])
+        starts[d] = int(r["Start_Timestamp"])
+        durs[d] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    per = collections.defaultdict(list)
+    for d in sorted(vals, key=lambda x: starts.get(x, x)):
+        per[names[d]].append((durs.get(d, 0), vals[d]))
+    counters = sorted({c for v in vals.values() for c in v})
+    lines = [f"# rocprofv3 counters per kernel, workload {name}; averages over the {steps} timed "
+             "steps (warm-up dispatches left out)",
+             f"# command (from /tmp): rocprofv3 --kernel-trace --pmc {' '.join(counters)} "
+             f"--output-format csv -d <dir> -o run -- {command}",
+             f"# the same run's bench.py line: ms_per_step (median) {b['ms_per_step']}",
+             "# kernel: average us, then counter = value per dispatch"]
+    for k, recs in per.items():
+        per_step = len(recs) // (steps + warm) if len(recs) >= steps + warm else 0
+        if per_step == 0 or k.startswith("__amd") or "copyBuffer" in k or "at::" in k:
+            continue
+        timed = recs[warm * per_step:(warm + steps) * per_step]
+        dur = sum(x[0] for x in timed) / len(timed)
+        avg = {c: sum(x[1].get(c, 0.0) for x in timed) / len(timed) for c in counters}
+        lines.append(f"{_short(k)}: {dur / 1e3:.1f} us")
+        lines.append("    " + "  ".join(f"{c}={v:.4g}" for c, v in avg.items()))
+        derived = []
+        if avg.get("TCC_HIT_sum", 0) + avg.get("TCC_MISS_sum", 0) > 0:
+            derived.append("L2 hit rate %.3f"
+                           % (avg["TCC_HIT_sum"] / (avg["TCC_HIT_sum"] + avg["TCC_MISS_sum"])))
+        if avg.get("SQ_LDS_IDX_ACTIVE", 0) > 0:
+            derived.append("LDS bank-conflict cycles / LDS active cycles %.4f"
+                           % (avg.get("SQ_LDS_BANK_CONFLICT", 0) / avg["SQ_LDS_IDX_ACTIVE"]))
+            derived.append("LDS data-FIFO-full cycles / LDS active cycles %.4f"
+                           % (avg.get("SQ_LDS_DATA_FIFO_FULL", 0) / avg["SQ_LDS_IDX_ACTIVE"]))
+        if avg.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) > 0 and "SQ_VALU_MFMA_COEXEC_CYCLES" in avg:
+            derived.append("VALU co-issued during MFMA-busy cycles %.3f"
+                           % (avg["SQ_VALU_MFMA_COEXEC_CYCLES"] / avg["SQ_VALU_MFMA_BUSY_CYCLES"]))
+        if avg.get("SQ_INSTS_LDS", 0) > 0 and "SQ_WAIT_INST_LDS" in avg:
+            derived.append("wave cycles waiting to issue LDS per LDS instruction %.2f"
+                           % (avg["SQ_WAIT_INST_LDS"] / avg["SQ_INSTS_LDS"]))
+        lines.extend("    " + x for x in derived)
+    text = "\n".join(lines) + "\n"
+    with open(os.path.join(PROFILES, f"{tag}_{name}.txt"), "w") as f:
+        f.write(text)
+    return text
+
+
 def summarize_sweep(logs, command: str) -> str:
     """Write profiles/sweep_sq_lvx_2k_128k.txt from bench.py lines of the
     headline workload at several S_Q (same S_KV, heads, D, shards)."""
@@ -378,6 +438,9 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("PMC_DIR", "BENCH_LOG"),
                     help="write profiles/mfma_busy_<workload>.txt from a rocprofv3 --pmc "
                          "--kernel-trace run and the bench line it printed, and exit")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("PMC_DIR", "BENCH_LOG", "TAG"),
+                    help="write profiles/<TAG>_<workload>.txt with every counter of a rocprofv3 "
+                         "--pmc --kernel-trace run, per kernel, and exit")
     ap.add_argument("--summarize-sweep", nargs="+", metavar="BENCH_LOG",
                     help="write profiles/sweep_sq_lvx_2k_128k.txt from bench lines at several "
                          "S_Q and exit")
@@ -404,6 +467,10 @@ def main():
         return
     if args.summarize_counters:
         print(summarize_counters(*args.summarize_counters, name, args.profiled_command))
+        return
+    if args.summarize_pmc:
+        d, log, tag = args.summarize_pmc
+        print(summarize_pmc(d, log, name, tag, args.profiled_command))
         return
     if args.summarize_sweep:
         print(summarize_sweep(args.summarize_sweep, args.profiled_command))
