@@ -319,7 +319,7 @@ def summarize_rounds(trace_dirs, labels, workload: str, n: int, command: str) ->
                 for r in rows if "fwd_bf16_kernel" in r["Kernel_Name"]][-n:]
         lines.append(f"{label:12s} " + " ".join(f"{x:6.2f}" for x in durs) + f"   sum {sum(durs):.2f}")
     text = "\n".join(lines) + "\n"
-    with open(os.path.join(ROOT, "profiles", f"rounds_{workload}.txt"), "w") as f:
+    with open(os.path.join(PROFILES, f"rounds_{workload}.txt"), "w") as f:
         f.write(text)
     return text
 
