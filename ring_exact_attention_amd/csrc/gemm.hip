@@ -18,11 +18,15 @@
 // LDS with rows padded by 16 bytes (conflict-free 16-byte operand reads).
 // Within a stage the 32 MFMAs of a wave are issued in a fixed order, the
 // operands of each 16-element k-step read during the previous one; the
-// chunks staged for the next stage go to the other buffer one every four
-// MFMAs, each followed two MFMAs later by the load (into the same registers)
-// of that chunk for the stage after it, which then has a whole stage to land.
-// Bursts of wide LDS writes fill the LDS data FIFO and stall every wave's
-// LDS reads; spreading them and the reads over the MFMAs is worth 14% here.
+// chunks staged for the next stage go to the other buffer one every three
+// MFMAs of the first three k-steps, each followed one MFMA later by the load
+// (into the same registers) of that chunk for the stage after it, which then
+// has a whole stage to land.  Bursts of wide LDS writes fill the LDS data
+// FIFO and stall every wave's LDS reads; spreading them and the reads over
+// the MFMAs is worth 14% here.  The stage's barrier comes before its last
+// k-step, whose operands are already in registers, so the next stage's first
+// operand reads overlap those MFMAs instead of idling the matrix core
+// after the barrier (2.5%).
 // Workgroups that share a y tile are placed consecutively on one XCD so the
 // tile is read from HBM once and served from that XCD's L2; W (both
 // projections, 64 MB) stays in the MALL.
@@ -131,26 +135,30 @@ __global__ __launch_bounds__(T::NT) void gemm_kv_kernel(GemmParams p) {
   };
 
   // One stage: the MFMAs of buffer buf in a fixed issue order, each k-step's
-  // operands read during the previous k-step, and (WR) the staged chunks of
-  // the next stage written into buf^1 one per MFMA, then (LD) the loads of
-  // the stage after it issued one per MFMA, so neither the LDS writes nor
-  // the global loads arrive in bursts.
-  static_assert(NM % KC == 0, "staging chunks spread evenly over a stage's MFMAs");
-  auto stage = [&](auto wr_, auto ld_, int buf, int e_next) __attribute__((always_inline)) {
+  // operands read during the previous k-step.  (WR) The staged chunks of the
+  // next stage are written into buf^1 over the first KSN-1 k-steps and (LD)
+  // the loads of the stage after it issued one after each write.  (NEXT) The
+  // workgroup barrier sits before the last k-step: every wave has written the
+  // next stage and read this one, so after it the next stage's first operands
+  // are read from buf^1 while the last k-step's MFMAs run on registers.
+  constexpr int NW_ = (KSN - 1) * T::FA * T::FB;  // MFMAs carrying the writes
+  static_assert(NW_ % KC == 0, "staging chunks spread evenly over the first k-steps");
+  bf16x8 op[2][NOP];
+  auto stage = [&](auto wr_, auto ld_, auto next_, int buf, int e_next) __attribute__((always_inline)) {
     constexpr bool WR = decltype(wr_)::value, LD = decltype(ld_)::value;
-    bf16x8 op[2][NOP];
-#pragma unroll
-    for (int o = 0; o < NOP; ++o) op[0][o] = rd(buf, 0, o);
+    constexpr bool NEXT = decltype(next_)::value;
     static_for<0, NM>([&](auto mi) __attribute__((always_inline)) {
       constexpr int m = decltype(mi)::value;
       constexpr int ks = m / (T::FA * T::FB), idx = m % (T::FA * T::FB);
       constexpr int a = idx / T::FB, b = idx % T::FB;
+      if constexpr (NEXT && m == NW_) __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
       acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[ks & 1][a], op[ks & 1][T::FA + b],
                                                           acc[a][b], 0, 0, 0);
       if constexpr (ks + 1 < KSN && idx < NOP) op[(ks + 1) & 1][idx] = rd(buf, ks + 1, idx);
-      if constexpr (WR && m % (NM / KC) == 0) store1(m / (NM / KC), buf ^ 1);
-      if constexpr (LD && m % (NM / KC) == (NM / KC) / 2) load1(m / (NM / KC), e_next);
+      if constexpr (NEXT && ks + 1 == KSN && idx < NOP) op[0][idx] = rd(buf ^ 1, 0, idx);
+      if constexpr (WR && m < NW_ && m % (NW_ / KC) == 0) store1(m / (NW_ / KC), buf ^ 1);
+      if constexpr (LD && m < NW_ && m % (NW_ / KC) == 1) load1(m / (NW_ / KC), e_next);
     });
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -168,17 +176,15 @@ __global__ __launch_bounds__(T::NT) void gemm_kv_kernel(GemmParams p) {
     for (int i = 0; i < KC; ++i) load1(i, GK);
   }
   __syncthreads();
+#pragma unroll
+  for (int o = 0; o < NOP; ++o) op[0][o] = rd(0, 0, o);
   int kt = 0;
-  for (; kt + 2 < nk; ++kt) {
-    stage(T_{}, T_{}, kt & 1, (kt + 2) * GK);
-    __syncthreads();
-  }
+  for (; kt + 2 < nk; ++kt) stage(T_{}, T_{}, T_{}, kt & 1, (kt + 2) * GK);
   if (kt + 1 < nk) {
-    stage(T_{}, F_{}, kt & 1, 0);
-    __syncthreads();
+    stage(T_{}, F_{}, T_{}, kt & 1, 0);
     ++kt;
   }
-  stage(F_{}, F_{}, kt & 1, 0);
+  stage(F_{}, F_{}, F_{}, kt & 1, 0);
 
   bf16* out = p.out[proj];
 #pragma unroll

@@ -8,7 +8,8 @@
 // Both are 256 x 256-tiled MFMA GEMMs on 8 waves (2 x 4, 128 x 64 per wave),
 // 64 contraction rows per LDS stage, double buffered, with the MFMAs of a
 // stage in a fixed order beside the operand reads of the next k-step, the
-// LDS writes of the next stage and the global loads of the one after.  An operand whose
+// LDS writes of the next stage and the global loads of the one after; the
+// stage's barrier precedes its last k-step (see mma_stage).  An operand whose
 // contraction index is its storage row (dK and y in the weight gradient, W^T
 // in dy) is staged row-major as [k][m] and read with ds_read_b64_tr_b16: each
 // lane takes rows k0..k0+3 and k0+4..k0+7 of its column, the same k order as
@@ -69,32 +70,38 @@ __device__ inline bf16x8 read_op(const bf16* As, const bf16* Bs, int ks, int o, 
 }
 
 // One stage of MFMAs from (As, Bs) in a fixed issue order, each k-step's
-// operands read during the previous one.  Chunk hooks run beside the MFMAs,
-// one of each every NM/NCH MFMAs: write(i) (the next stage's staged chunk i
-// into the other buffer), then load(i) (chunk i of the stage after it, into
-// the registers just written out), so neither LDS writes nor global loads
-// come in bursts and every load has a whole stage to land.
+// operands read during the previous one (op[0] holds the first k-step's on
+// entry).  Chunk hooks run beside the MFMAs of the first KSN-1 k-steps, one of
+// each every NW/NCH MFMAs: write(i) (the next stage's staged chunk i into the
+// other buffer), then load(i) (chunk i of the stage after it, into the
+// registers just written out), so neither LDS writes nor global loads come in
+// bursts and every load has a whole stage to land.  With NEXT the
+// workgroup's barrier sits before the last k-step (every wave has written
+// the next stage and read this one by then) and the next stage's first
+// operands are read from (Asn, Bsn) while the last k-step's MFMAs run on
+// registers.
 constexpr int NCH = 8;  // 16-byte staging chunks per thread and stage
-template <bool AT, bool WR, bool LD, typename W, typename L>
+constexpr int NOP = FA + FB;
+template <bool AT, bool WR, bool LD, bool NEXT, typename W, typename L>
 __device__ inline __attribute__((always_inline)) void mma_stage(
-    const bf16* As, const bf16* Bs, int wm, int wn, int lane, f32x16 (&acc)[FA][FB], W&& write,
-    L&& load) {
-  constexpr int NOP = FA + FB, KSN = TK / 16, NM = KSN * FA * FB;
-  static_assert(NM % NCH == 0, "staging chunks spread evenly over a stage's MFMAs");
-  bf16x8 op[2][NOP];
-#pragma unroll
-  for (int o = 0; o < NOP; ++o) op[0][o] = read_op<AT>(As, Bs, 0, o, wm, wn, lane);
+    const bf16* As, const bf16* Bs, const bf16* Asn, const bf16* Bsn, int wm, int wn, int lane,
+    f32x16 (&acc)[FA][FB], bf16x8 (&op)[2][NOP], W&& write, L&& load) {
+  constexpr int KSN = TK / 16, NM = KSN * FA * FB, NW = (KSN - 1) * FA * FB;
+  static_assert(NW % NCH == 0, "staging chunks spread evenly over the first k-steps");
   static_for<0, NM>([&](auto mi) __attribute__((always_inline)) {
     constexpr int m = decltype(mi)::value;
     constexpr int ks = m / (FA * FB), idx = m % (FA * FB);
     constexpr int a = idx / FB, b = idx % FB;
+    if constexpr (NEXT && m == NW) __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[ks & 1][a], op[ks & 1][FA + b],
                                                         acc[a][b], 0, 0, 0);
     if constexpr (ks + 1 < KSN && idx < NOP)
       op[(ks + 1) & 1][idx] = read_op<AT>(As, Bs, ks + 1, idx, wm, wn, lane);
-    if constexpr (WR && m % (NM / NCH) == 0) write(m / (NM / NCH));
-    if constexpr (LD && m % (NM / NCH) == (NM / NCH) / 2) load(m / (NM / NCH));
+    if constexpr (NEXT && ks + 1 == KSN && idx < NOP)
+      op[0][idx] = read_op<AT>(Asn, Bsn, 0, idx, wm, wn, lane);
+    if constexpr (WR && m < NW && m % (NW / NCH) == 0) write(m / (NW / NCH));
+    if constexpr (LD && m < NW && m % (NW / NCH) == 1) load(m / (NW / NCH));
   });
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -179,26 +186,28 @@ __global__ __launch_bounds__(NT) void gemm_dw_kernel(GradParams p) {
     for (int i = 0; i < NCH; ++i) load1(i);
   }
   __syncthreads();
+  bf16x8 op[2][NOP];
+#pragma unroll
+  for (int o = 0; o < NOP; ++o) op[0][o] = read_op<true>(smem, smem + T_EL, 0, o, wm, wn, lane);
   int64_t kt = 0;
   for (; kt + 2 < nk; ++kt) {
     const int buf = (int)(kt & 1);
-    const bf16* As = smem + buf * 2 * T_EL;
+    const bf16 *As = smem + buf * 2 * T_EL, *An = smem + (buf ^ 1) * 2 * T_EL;
     aim((kt + 2) * TK);
-    mma_stage<true, true, true>(As, As + T_EL, wm, wn, lane, acc,
-                                [&](int i) { store1(i, buf ^ 1); }, load1);
-    __syncthreads();
+    mma_stage<true, true, true, true>(As, As + T_EL, An, An + T_EL, wm, wn, lane, acc, op,
+                                      [&](int i) { store1(i, buf ^ 1); }, load1);
   }
   if (kt + 1 < nk) {
     const int buf = (int)(kt & 1);
-    const bf16* As = smem + buf * 2 * T_EL;
-    mma_stage<true, true, false>(As, As + T_EL, wm, wn, lane, acc,
-                                 [&](int i) { store1(i, buf ^ 1); }, load1);
-    __syncthreads();
+    const bf16 *As = smem + buf * 2 * T_EL, *An = smem + (buf ^ 1) * 2 * T_EL;
+    mma_stage<true, true, false, true>(As, As + T_EL, An, An + T_EL, wm, wn, lane, acc, op,
+                                       [&](int i) { store1(i, buf ^ 1); }, load1);
     ++kt;
   }
   {
     const bf16* As = smem + (int)(kt & 1) * 2 * T_EL;
-    mma_stage<true, false, false>(As, As + T_EL, wm, wn, lane, acc, load1, load1);
+    mma_stage<true, false, false, false>(As, As + T_EL, As, As + T_EL, wm, wn, lane, acc, op,
+                                         load1, load1);
   }
   store_tile(p.dwt[proj], p.E, n0, p.HD, e0, wm, wn, lane, p.accumulate != 0, acc);
 }
@@ -263,26 +272,28 @@ __global__ __launch_bounds__(NT) void gemm_dy_kernel(GradParams p) {
     for (int i = 0; i < NCH; ++i) load1(i);
   }
   __syncthreads();
+  bf16x8 op[2][NOP];
+#pragma unroll
+  for (int o = 0; o < NOP; ++o) op[0][o] = read_op<false>(smem, smem + N_EL, 0, o, wm, wn, lane);
   int kt = 0;
   for (; kt + 2 < nk; ++kt) {
     const int buf = kt & 1;
-    const bf16* As = smem + buf * (N_EL + T_EL);
+    const bf16 *As = smem + buf * (N_EL + T_EL), *An = smem + (buf ^ 1) * (N_EL + T_EL);
     aim(kt + 2);
-    mma_stage<false, true, true>(As, As + N_EL, wm, wn, lane, acc,
-                                 [&](int i) { store1(i, buf ^ 1); }, load1);
-    __syncthreads();
+    mma_stage<false, true, true, true>(As, As + N_EL, An, An + N_EL, wm, wn, lane, acc, op,
+                                       [&](int i) { store1(i, buf ^ 1); }, load1);
   }
   if (kt + 1 < nk) {
     const int buf = kt & 1;
-    const bf16* As = smem + buf * (N_EL + T_EL);
-    mma_stage<false, true, false>(As, As + N_EL, wm, wn, lane, acc,
-                                  [&](int i) { store1(i, buf ^ 1); }, load1);
-    __syncthreads();
+    const bf16 *As = smem + buf * (N_EL + T_EL), *An = smem + (buf ^ 1) * (N_EL + T_EL);
+    mma_stage<false, true, false, true>(As, As + N_EL, An, An + N_EL, wm, wn, lane, acc, op,
+                                        [&](int i) { store1(i, buf ^ 1); }, load1);
     ++kt;
   }
   {
     const bf16* As = smem + (kt & 1) * (N_EL + T_EL);
-    mma_stage<false, false, false>(As, As + N_EL, wm, wn, lane, acc, load1, load1);
+    mma_stage<false, false, false, false>(As, As + N_EL, As, As + N_EL, wm, wn, lane, acc, op,
+                                          load1, load1);
   }
   store_tile(p.dy, p.E, m0, M, e0, wm, wn, lane, p.accumulate != 0, acc);
 }
