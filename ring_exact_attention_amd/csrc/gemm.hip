@@ -7,26 +7,35 @@
 //   as w_t[n, e] (n = h*D + d), the [out, in] layout of a linear layer.
 //
 // The kernel computes the transposed product C^T[n, s] = w_t[n, :] . y[s, :]
-// on v_mfma_f32_32x32x16_bf16, so that each lane of a 32x32 output block owns
+// on v_mfma_f32_16x16x32_bf16, so that each lane of a 16x16 output block owns
 // four consecutive n (= four consecutive head dims d) of one key row s and
 // stores them as one 8-byte write into the [B, H, S, D] output.  Both
 // operands keep the contraction index e contiguous in memory and in LDS.
 //
 // Tiling: 256 (n) x 256 (s) per workgroup of 8 waves (2 x 4, two per SIMD),
-// 128 x 64 per wave (4 x 2 MFMA blocks, fp32 accumulators), 64 e per LDS
+// 128 x 64 per wave (8 x 4 MFMA blocks, fp32 accumulators), 64 e per LDS
 // stage (128 contiguous bytes per row and load), double buffered in 144 KB of
 // LDS with rows padded by 16 bytes (conflict-free 16-byte operand reads).
-// Within a stage the 32 MFMAs of a wave are issued in a fixed order, the
-// operands of each 16-element k-step read during the previous one; the
-// chunks staged for the next stage go to the other buffer one every three
-// MFMAs of the first three k-steps, each followed one MFMA later by the load
-// (into the same registers) of that chunk for the stage after it, which then
-// has a whole stage to land.  Bursts of wide LDS writes fill the LDS data
-// FIFO and stall every wave's LDS reads; spreading them and the reads over
-// the MFMAs is worth 14% here.  The stage's barrier comes before its last
-// k-step, whose operands are already in registers, so the next stage's first
-// operand reads overlap those MFMAs instead of idling the matrix core
-// after the barrier (2.5%).
+// Within a stage the 64 MFMAs of a wave are issued in a fixed order, rows of
+// blocks one after the other: a row's A operand is read while the row before
+// it runs, and the B operands of the next 32-element k-step during the second
+// half of the current one.  The chunks staged for the next stage go to the
+// other buffer one every four MFMAs of the first k-step, each followed one
+// MFMA later by the load (into the same registers) of that chunk for the
+// stage after it, which then has a whole stage to land.  Bursts of wide LDS
+// writes fill the LDS data FIFO and stall every wave's LDS reads; spreading
+// them and the reads over the MFMAs is worth 14% here.  The stage's barrier
+// comes before its last k-step, whose operands are already in registers, so
+// the next stage's first operand reads overlap those MFMAs instead of idling
+// the matrix core after the barrier.
+//
+// The 16x16x32 MFMA rather than 32x32x16: under sustained load the chip's
+// clock is set by its power draw, and per FLOP the smaller block moves half
+// the accumulator data through the register file.  Measured on the recompute
+// shape, the same MFMA-busy cycles ran at 1.87 against 1.67 GHz, 2-3% faster
+// overall, with identical results (each block is a sum over e in the same
+// order).
+//
 // Workgroups that share a y tile are placed consecutively on one XCD so the
 // tile is read from HBM once and served from that XCD's L2; W (both
 // projections, 64 MB) stays in the MALL.
@@ -59,7 +68,7 @@ struct GemmTile {
   static constexpr int GM = GM_, GN = GN_, GK = GK_, WM = WM_, WN = WN_;
   static constexpr int NW = WM * WN, NT = 64 * NW;
   static constexpr int WTM = GM / WM, WTN = GN / WN;  // per-wave tile (n x s)
-  static constexpr int FA = WTM / 32, FB = WTN / 32;  // 32x32 MFMA blocks per wave
+  static constexpr int FA = WTM / 16, FB = WTN / 16;  // 16x16 MFMA blocks per wave
   static constexpr int GS = GK + 8;                   // LDS row stride (elements)
   static constexpr int A_EL = GM * GS, B_EL = GN * GS;
   static constexpr int CPR = GK / 8;                  // 16-byte chunks per row
@@ -80,7 +89,7 @@ __global__ __launch_bounds__(T::NT) void gemm_kv_kernel(GemmParams p) {
   const int st = grp % p.s_tiles;
   const int n0 = nt * GM, s0 = st * GN;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave / T::WN, wn = wave % T::WN;
   const bf16* wsrc = p.w[proj];
 
@@ -89,23 +98,22 @@ __global__ __launch_bounds__(T::NT) void gemm_kv_kernel(GemmParams p) {
   // the end repeat the last row.  Byte offsets from the operand's base fit in
   // 32 bits (rows x E x 2 < 2^31, checked on the host).
   uint32_t goff[KC];
-  bf16* sdst[KC];
+  int sdst[KC];  // LDS element offsets
   const bf16* ysrc = p.y;
 #pragma unroll
   for (int i = 0; i < KC; ++i) {
     const int c = tid + T::NT * i;
-    bf16* As0 = smem;
     if (i < KA) {
       const int row = c / CPR, col8 = c % CPR;
       const int n = min(n0 + row, p.HD - 1);
       goff[i] = ((uint32_t)n * (uint32_t)p.E + (uint32_t)(col8 * 8)) * 2u;
-      sdst[i] = As0 + row * GS + col8 * 8;
+      sdst[i] = row * GS + col8 * 8;
     } else {
       const int cb = c - GM * CPR;
       const int row = cb / CPR, col8 = cb % CPR;
       const int sr = min(s0 + row, p.BS - 1);
       goff[i] = ((uint32_t)sr * (uint32_t)p.E + (uint32_t)(col8 * 8)) * 2u;
-      sdst[i] = As0 + T::A_EL + row * GS + col8 * 8;
+      sdst[i] = T::A_EL + row * GS + col8 * 8;
     }
   }
   u32x4 stg[KC];
@@ -114,28 +122,29 @@ __global__ __launch_bounds__(T::NT) void gemm_kv_kernel(GemmParams p) {
     stg[i] = *(const u32x4*)(base + goff[i]);
   };
   auto store1 = [&](int i, int buf) __attribute__((always_inline)) {
-    *(u32x4*)(sdst[i] + buf * (T::A_EL + T::B_EL)) = stg[i];
+    *(u32x4*)(smem + sdst[i] + buf * (T::A_EL + T::B_EL)) = stg[i];
   };
 
-  f32x16 acc[T::FA][T::FB];
+  f32x4 acc[T::FA][T::FB];
 #pragma unroll
   for (int a = 0; a < T::FA; ++a)
 #pragma unroll
-    for (int b = 0; b < T::FB; ++b) acc[a][b] = f32x16{};
+    for (int b = 0; b < T::FB; ++b) acc[a][b] = f32x4{};
 
   // operand reads: A rows (n) of this wave's block a, B rows (s) of block b,
-  // 16 contraction elements at step ks
-  const bf16* aread = smem + (wm * T::WTM + lr) * GS + 8 * g;
-  const bf16* bread = smem + T::A_EL + (wn * T::WTN + lr) * GS + 8 * g;
-  constexpr int NOP = T::FA + T::FB, KSN = GK / 16, NM = KSN * T::FA * T::FB;
+  // 32 contraction elements at step ks (lane: row lane%16, elements 8*(lane/16) on)
+  const int l16 = lane & 15, q4 = lane >> 4;
+  const bf16* aread = smem + (wm * T::WTM + l16) * GS + 8 * q4;
+  const bf16* bread = smem + T::A_EL + (wn * T::WTN + l16) * GS + 8 * q4;
+  constexpr int KSN = GK / 32, NM = KSN * T::FA * T::FB;
   auto rd = [&](int buf, int ks, int o) __attribute__((always_inline)) {
-    const int bo = buf * (T::A_EL + T::B_EL) + 16 * ks;
-    return o < T::FA ? *(const bf16x8*)(aread + bo + 32 * o * GS)
-                     : *(const bf16x8*)(bread + bo + 32 * (o - T::FA) * GS);
+    const int bo = buf * (T::A_EL + T::B_EL) + 32 * ks;
+    return o < T::FA ? *(const bf16x8*)(aread + bo + 16 * o * GS)
+                     : *(const bf16x8*)(bread + bo + 16 * (o - T::FA) * GS);
   };
 
-  // One stage: the MFMAs of buffer buf in a fixed issue order, each k-step's
-  // operands read during the previous k-step.  (WR) The staged chunks of the
+  // One stage: the MFMAs of buffer buf in a fixed issue order (block rows
+  // a-major), operands read ahead as described above.  (WR) The staged chunks of the
   // next stage are written into buf^1 over the first KSN-1 k-steps and (LD)
   // the loads of the stage after it issued one after each write.  (NEXT) The
   // workgroup barrier sits before the last k-step: every wave has written the
@@ -143,7 +152,10 @@ __global__ __launch_bounds__(T::NT) void gemm_kv_kernel(GemmParams p) {
   // are read from buf^1 while the last k-step's MFMAs run on registers.
   constexpr int NW_ = (KSN - 1) * T::FA * T::FB;  // MFMAs carrying the writes
   static_assert(NW_ % KC == 0, "staging chunks spread evenly over the first k-steps");
-  bf16x8 op[2][NOP];
+  static_assert(T::FA % 2 == 0, "A rows alternate between two registers");
+  // operands: the A block of the current row and the next (rows a-major),
+  // all B blocks of the current k-step and of the next
+  bf16x8 abuf[2], bbuf[2][T::FB];
   auto stage = [&](auto wr_, auto ld_, auto next_, int buf, int e_next) __attribute__((always_inline)) {
     constexpr bool WR = decltype(wr_)::value, LD = decltype(ld_)::value;
     constexpr bool NEXT = decltype(next_)::value;
@@ -153,10 +165,16 @@ __global__ __launch_bounds__(T::NT) void gemm_kv_kernel(GemmParams p) {
       constexpr int a = idx / T::FB, b = idx % T::FB;
       if constexpr (NEXT && m == NW_) __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
-      acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[ks & 1][a], op[ks & 1][T::FA + b],
-                                                          acc[a][b], 0, 0, 0);
-      if constexpr (ks + 1 < KSN && idx < NOP) op[(ks + 1) & 1][idx] = rd(buf, ks + 1, idx);
-      if constexpr (NEXT && ks + 1 == KSN && idx < NOP) op[0][idx] = rd(buf ^ 1, 0, idx);
+      acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[a & 1], bbuf[ks & 1][b], acc[a][b], 0, 0, 0);
+      if constexpr (b == 0) {  // the next row's A block
+        if constexpr (a + 1 < T::FA) abuf[(a + 1) & 1] = rd(buf, ks, a + 1);
+        else if constexpr (ks + 1 < KSN) abuf[0] = rd(buf, ks + 1, 0);
+        else if constexpr (NEXT) abuf[0] = rd(buf ^ 1, 0, 0);
+      }
+      if constexpr (a == T::FA / 2) {  // the next k-step's B block b
+        if constexpr (ks + 1 < KSN) bbuf[(ks + 1) & 1][b] = rd(buf, ks + 1, T::FA + b);
+        else if constexpr (NEXT) bbuf[0][b] = rd(buf ^ 1, 0, T::FA + b);
+      }
       if constexpr (WR && m < NW_ && m % (NW_ / KC) == 0) store1(m / (NW_ / KC), buf ^ 1);
       if constexpr (LD && m < NW_ && m % (NW_ / KC) == 1) load1(m / (NW_ / KC), e_next);
     });
@@ -176,8 +194,9 @@ __global__ __launch_bounds__(T::NT) void gemm_kv_kernel(GemmParams p) {
     for (int i = 0; i < KC; ++i) load1(i, GK);
   }
   __syncthreads();
+  abuf[0] = rd(0, 0, 0);
 #pragma unroll
-  for (int o = 0; o < NOP; ++o) op[0][o] = rd(0, 0, o);
+  for (int o = 0; o < T::FB; ++o) bbuf[0][o] = rd(0, 0, T::FA + o);
   int kt = 0;
   for (; kt + 2 < nk; ++kt) stage(T_{}, T_{}, T_{}, kt & 1, (kt + 2) * GK);
   if (kt + 1 < nk) {
@@ -189,20 +208,17 @@ __global__ __launch_bounds__(T::NT) void gemm_kv_kernel(GemmParams p) {
   bf16* out = p.out[proj];
 #pragma unroll
   for (int b = 0; b < T::FB; ++b) {
-    const int s = s0 + wn * T::WTN + 32 * b + lr;
+    const int s = s0 + wn * T::WTN + 16 * b + l16;
     if (s >= p.BS) continue;
     const int bb = s / p.S, si = s % p.S;
 #pragma unroll
-    for (int a = 0; a < T::FA; ++a)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = n0 + wm * T::WTM + 32 * a + 8 * i + 4 * g;
-        if (n >= p.HD) continue;
-        const int hh = n / p.D, d = n % p.D;
-        bf16* dst = out + bb * p.so[proj][0] + hh * p.so[proj][1] + (int64_t)si * p.so[proj][2] + d;
-        *(u32x2*)dst = u32x2{pk(acc[a][b][4 * i], acc[a][b][4 * i + 1]),
-                             pk(acc[a][b][4 * i + 2], acc[a][b][4 * i + 3])};
-      }
+    for (int a = 0; a < T::FA; ++a) {
+      const int n = n0 + wm * T::WTM + 16 * a + 4 * q4;
+      if (n >= p.HD) continue;
+      const int hh = n / p.D, d = n % p.D;
+      bf16* dst = out + bb * p.so[proj][0] + hh * p.so[proj][1] + (int64_t)si * p.so[proj][2] + d;
+      *(u32x2*)dst = u32x2{pk(acc[a][b][0], acc[a][b][1]), pk(acc[a][b][2], acc[a][b][3])};
+    }
   }
 }
 
