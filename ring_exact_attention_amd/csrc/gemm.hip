@@ -14,20 +14,21 @@
 //
 // Tiling: 256 (n) x 256 (s) per workgroup of 8 waves (2 x 4, two per SIMD),
 // 128 x 64 per wave (8 x 4 MFMA blocks, fp32 accumulators), 64 e per LDS
-// stage (128 contiguous bytes per row and load), double buffered in 144 KB of
-// LDS with rows padded by 16 bytes (conflict-free 16-byte operand reads).
+// stage (128 contiguous bytes per row and load), double buffered in 160 KB of
+// LDS with rows padded by 32 bytes: rows 160 bytes apart (an odd multiple of
+// 32 mod 256) keep the 16-byte operand reads of the 16x16x32 layout free of
+// bank conflicts, where 144-byte rows conflicted in 37% of the LDS cycles.
 // Within a stage the 64 MFMAs of a wave are issued in a fixed order, rows of
-// blocks one after the other: a row's A operand is read while the row before
-// it runs, and the B operands of the next 32-element k-step during the second
-// half of the current one.  The chunks staged for the next stage go to the
+// blocks one after the other: a row's A operand is read three rows ahead, and
+// the B operands of the next 32-element k-step while its row 5 runs.  The chunks staged for the next stage go to the
 // other buffer one every four MFMAs of the first k-step, each followed one
 // MFMA later by the load (into the same registers) of that chunk for the
 // stage after it, which then has a whole stage to land.  Bursts of wide LDS
 // writes fill the LDS data FIFO and stall every wave's LDS reads; spreading
 // them and the reads over the MFMAs is worth 14% here.  The stage's barrier
-// comes before its last k-step, whose operands are already in registers, so
-// the next stage's first operand reads overlap those MFMAs instead of idling
-// the matrix core after the barrier.
+// comes before the last three block rows, whose operands are already in
+// registers, so the next stage's first operand reads overlap those MFMAs
+// instead of idling the matrix core after the barrier.
 //
 // The 16x16x32 MFMA rather than 32x32x16: under sustained load the chip's
 // clock is set by its power draw, and per FLOP the smaller block moves half
@@ -69,7 +70,7 @@ struct GemmTile {
   static constexpr int NW = WM * WN, NT = 64 * NW;
   static constexpr int WTM = GM / WM, WTN = GN / WN;  // per-wave tile (n x s)
   static constexpr int FA = WTM / 16, FB = WTN / 16;  // 16x16 MFMA blocks per wave
-  static constexpr int GS = GK + 8;                   // LDS row stride (elements)
+  static constexpr int GS = GK + 16;                  // LDS row stride (elements)
   static constexpr int A_EL = GM * GS, B_EL = GN * GS;
   static constexpr int CPR = GK / 8;                  // 16-byte chunks per row
   static constexpr int KC = (GM + GN) * CPR / NT;     // chunks per thread per stage
@@ -143,35 +144,43 @@ __global__ __launch_bounds__(T::NT) void gemm_kv_kernel(GemmParams p) {
                      : *(const bf16x8*)(bread + bo + 16 * (o - T::FA) * GS);
   };
 
-  // One stage: the MFMAs of buffer buf in a fixed issue order (block rows
-  // a-major), operands read ahead as described above.  (WR) The staged chunks of the
-  // next stage are written into buf^1 over the first KSN-1 k-steps and (LD)
-  // the loads of the stage after it issued one after each write.  (NEXT) The
-  // workgroup barrier sits before the last k-step: every wave has written the
-  // next stage and read this one, so after it the next stage's first operands
-  // are read from buf^1 while the last k-step's MFMAs run on registers.
+  // One stage: the MFMAs of buffer buf in a fixed issue order, block rows
+  // a-major over its KSN k-steps; a row's A block is read AD rows ahead, the
+  // next k-step's B blocks while row XR of the current one runs.  (WR) The
+  // staged chunks of the next stage are written into buf^1 over the first
+  // KSN-1 k-steps and (LD) the loads of the stage after it issued one after
+  // each write.  (NEXT) The workgroup barrier sits before row XR of the last
+  // k-step: by then every wave has written the next stage and issued its last
+  // read of this one (the A blocks of the rows after it are AD rows ahead),
+  // so after it the next stage's first operands are read from buf^1 while
+  // the last AD rows' MFMAs run on registers, and no wave writes buf (in the
+  // next stage) while another still reads it.
   constexpr int NW_ = (KSN - 1) * T::FA * T::FB;  // MFMAs carrying the writes
   static_assert(NW_ % KC == 0, "staging chunks spread evenly over the first k-steps");
-  static_assert(T::FA % 2 == 0, "A rows alternate between two registers");
-  // operands: the A block of the current row and the next (rows a-major),
+  constexpr int AD = 3, NAB = 4, XR = T::FA - AD;
+  static_assert(AD < NAB && (KSN * T::FA) % NAB == 0 && XR >= AD,
+                "A registers rotate evenly over stages; rows after the barrier read before it");
+  constexpr int NX = NM - AD * T::FB;  // the barrier's place in a NEXT stage
+  static_assert(NX >= NW_, "the next stage's chunks are written before the barrier");
+  // operands: the A blocks of rows r .. r+AD (rows counted over the stage),
   // all B blocks of the current k-step and of the next
-  bf16x8 abuf[2], bbuf[2][T::FB];
+  bf16x8 abuf[NAB], bbuf[2][T::FB];
   auto stage = [&](auto wr_, auto ld_, auto next_, int buf, int e_next) __attribute__((always_inline)) {
     constexpr bool WR = decltype(wr_)::value, LD = decltype(ld_)::value;
     constexpr bool NEXT = decltype(next_)::value;
     static_for<0, NM>([&](auto mi) __attribute__((always_inline)) {
       constexpr int m = decltype(mi)::value;
       constexpr int ks = m / (T::FA * T::FB), idx = m % (T::FA * T::FB);
-      constexpr int a = idx / T::FB, b = idx % T::FB;
-      if constexpr (NEXT && m == NW_) __syncthreads();
+      constexpr int a = idx / T::FB, b = idx % T::FB, r = ks * T::FA + a;
+      if constexpr (NEXT && m == NX) __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
-      acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[a & 1], bbuf[ks & 1][b], acc[a][b], 0, 0, 0);
-      if constexpr (b == 0) {  // the next row's A block
-        if constexpr (a + 1 < T::FA) abuf[(a + 1) & 1] = rd(buf, ks, a + 1);
-        else if constexpr (ks + 1 < KSN) abuf[0] = rd(buf, ks + 1, 0);
-        else if constexpr (NEXT) abuf[0] = rd(buf ^ 1, 0, 0);
+      acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abuf[r % NAB], bbuf[ks & 1][b], acc[a][b], 0, 0, 0);
+      if constexpr (b == 0) {  // the A block AD rows on
+        constexpr int r2 = r + AD;
+        if constexpr (r2 < KSN * T::FA) abuf[r2 % NAB] = rd(buf, r2 / T::FA, r2 % T::FA);
+        else if constexpr (NEXT) abuf[r2 % NAB] = rd(buf ^ 1, 0, r2 - KSN * T::FA);
       }
-      if constexpr (a == T::FA / 2) {  // the next k-step's B block b
+      if constexpr (a == XR) {  // the next k-step's B block b
         if constexpr (ks + 1 < KSN) bbuf[(ks + 1) & 1][b] = rd(buf, ks + 1, T::FA + b);
         else if constexpr (NEXT) bbuf[0][b] = rd(buf ^ 1, 0, T::FA + b);
       }
@@ -194,7 +203,8 @@ __global__ __launch_bounds__(T::NT) void gemm_kv_kernel(GemmParams p) {
     for (int i = 0; i < KC; ++i) load1(i, GK);
   }
   __syncthreads();
-  abuf[0] = rd(0, 0, 0);
+#pragma unroll
+  for (int o = 0; o < AD; ++o) abuf[o] = rd(0, 0, o);
 #pragma unroll
   for (int o = 0; o < T::FB; ++o) bbuf[0][o] = rd(0, 0, T::FA + o);
   int kt = 0;
