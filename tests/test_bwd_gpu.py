@@ -123,6 +123,25 @@ def test_kv_recompute_repeatable(bwa):
         assert torch.equal(k, k0) and torch.equal(v, v0)
 
 
+def test_kv_recompute_bwd_repeatable(bwa):
+    """dW_k^T, dW_v^T and dy at 16384 keys, E = 4096, 32 heads of 128, run three
+    times: bitwise the same results (fixed-order fp32 sums; a difference would be
+    an LDS stage read after another wave overwrote it)."""
+    B, S, E, H, D = 1, 16384, 4096, 32, 128
+    g = torch.Generator(device="cuda").manual_seed(11)
+    y = (torch.randn(B, S, E, device="cuda", generator=g) * 0.02).bfloat16()
+    wk = (torch.randn(H * D, E, device="cuda", generator=g) * 0.02).bfloat16()
+    wv = (torch.randn(H * D, E, device="cuda", generator=g) * 0.02).bfloat16()
+    dk = torch.randn(B, H, S, D, device="cuda", generator=g).bfloat16()
+    dv = torch.randn(B, H, S, D, device="cuda", generator=g).bfloat16()
+    log_case(stage="repeated gradient GEMMs", shape=(B, S, E, H, D))
+    ref = [t.clone() for t in bwa.bwa_kv_recompute_bwd(y, wk, wv, dk, dv)]
+    for _ in range(2):
+        got = bwa.bwa_kv_recompute_bwd(y, wk, wv, dk, dv)
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(got, ref))
+
+
 def test_kv_recompute_strided_output(bwa, orc):
     """Write K into a [B, S, H, D] buffer through strides."""
     B, S, E, H, D = 1, 200, 128, 2, 128
