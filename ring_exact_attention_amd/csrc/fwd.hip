@@ -110,36 +110,77 @@ __device__ inline void store4<bf16>(bf16* dst, float a, float b, float c, float 
 // SIMD is in its MFMA phase while the other is in its VALU phase, so the
 // matrix core and the vector ALU work at the same time.  Barrier intervals
 // ("slots") are numbered from 0; group A runs
-//   slot 0: S(0);  slot 2j+1: softmax(j) + write K(j+1);  slot 2j+2: PV(j) + S(j+1)
-// and group B runs the same sequence one slot later (writing V(j+1) in its
-// softmax slot).  K/V tiles rotate through three LDS buffers; a tile is read
-// from slot 2j to slot 2j+3 and the buffer it overwrites was last read two
-// slots earlier.  Each thread of a group stages KC 16-byte chunks of a tile:
-// loaded from global memory one softmax slot ahead, written to LDS in the next.
+//   slot 0: S(0);  slot 2j+1: softmax(j), load K(j+2);  slot 2j+2: PV(j) + S(j+1)
+// and group B runs the same sequence one slot later (loading V(j+2) in its
+// softmax slot).  K/V tiles rotate through three LDS buffers (tile j in buffer
+// j mod 3) and move from global memory to LDS directly (global_load_lds, no
+// registers).  Tile j's K is read in slots 2j and 2j+1 and its V in slots
+// 2j+2 and 2j+3, so K(j+2) may land in slot 2j+1 (K(j-1) was last read in
+// slot 2j-1) and V(j+2) in slot 2j+2 (V(j-1) last read in slot 2j+1).  A
+// group waits for its loads of tile j+1 in its next softmax slot, before the
+// barrier after which the tile is read.
 
 template <int D_>
 struct Bf16Fwd {
   static constexpr int D = D_, NW = 8, NT = 512, BM = 256, BN = 64;
-  // Padded LDS row strides (elements).  K rows are read 16 bytes per lane by
-  // ds_read_b128.  A transposing V read covers 8 rows x 64 bytes and is served
-  // 32 lanes (4 rows) at a time from 64 banks of 4 bytes: rows 2*(D+32) bytes
-  // apart land in distinct 64-byte quarters of the bank space (the stride is
-  // 64 or 192 mod 256), so the read is conflict-free; D+16 would pair rows
-  // on the same banks and halve the read rate.
-  static constexpr int KS = D + 8, VS = D + 32;
-  static constexpr int K_TILE = BN * KS, V_TILE = BN * VS;
+  // K and V tiles go from global memory straight to LDS, one 1 KB block (RPB
+  // rows of ROWB bytes) per wave and load instruction, so rows are unpadded
+  // inside a block and blocks are padded: K blocks by 32 bytes, V blocks by
+  // 64 (byte strides KB, VB).  Key order in a tile is permuted (kperm below)
+  // so that both read patterns are free of bank conflicts:
+  //   K, ds_read_b128, eight lanes at a time: lanes 0-7 read eight blocks,
+  //     32 bytes apart in the bank space;
+  //   V, ds_read_b64_tr_b16, 32 lanes at a time over 4 rows x 64 bytes: the
+  //     four rows lie in four blocks, 64 bytes apart in the bank space.
+  static constexpr int ROWB = 2 * D, RPB = 1024 / ROWB, NBK = BN / RPB, NBU = NBK / 2;
+  static constexpr int KB = 1024 + 32, VB = 1024 + 64;
+  static constexpr int K_TILE = NBK * KB, V_TILE = NBK * VB;  // bytes
   static constexpr int STAGE = K_TILE + V_TILE;
   static constexpr int NBUF = 3;
-  static constexpr int GT = NT / 2;                // threads per group
-  static constexpr int KC = (BN * D / 8) / GT;     // 16-byte chunks per staging thread
-  static_assert(KC * GT == BN * D / 8, "staging must divide evenly");
+  static constexpr int GT = NT / 2;  // threads per group
+  static constexpr int KC = NBK / 4;  // blocks per wave and tile (four waves per group)
+  static_assert(RPB * NBU == 32 && KC * 4 == NBK, "tile geometry");
 };
+
+// Tile row (key offset) held by row m of block pair u of the MFMA operands:
+// storage block (m mod NBU) + NBU u, row m / NBU of that block.
+template <int D>
+__device__ constexpr int kperm(int u, int m) {
+  using C = Bf16Fwd<D>;
+  return C::RPB * (m % C::NBU) + 32 * u + m / C::NBU;
+}
+
+// Barrier without the memory fence of __syncthreads: direct-to-LDS loads
+// stay in flight across it (their completion is awaited explicitly before the
+// barrier that publishes them); this wave's LDS reads are complete first.
+__device__ inline void slot_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// One direct global->LDS load: 16 bytes per lane from gaddr to LDS byte
+// address lds + 16 * lane (lds wave-uniform, passed in m0).  Issued from asm
+// so that the compiler adds no waits of its own for it; every read of the
+// loaded data follows an explicit wait_vm and a barrier.  Nothing else in the
+// kernel keeps a value in m0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved: the asm sets it itself
+__device__ inline void dma16(const void* gaddr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ inline uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 template <int D_>
 __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
   using C = Bf16Fwd<D_>;
-  constexpr int D = C::D, BN = C::BN, KS = C::KS, VS = C::VS;
-  __shared__ __attribute__((aligned(16))) bf16 smem[C::NBUF * C::STAGE];
+  constexpr int D = C::D, BN = C::BN;
+  __shared__ __attribute__((aligned(16))) char smem[C::NBUF * C::STAGE];
 
   Job jb;
   if (!make_job(p, C::BM, &jb)) return;
@@ -150,7 +191,6 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
   const int lr = lane & 31;
   const int g = lane >> 5;
   const bool groupB = wave >= 4;
-  const int gtid = tid & (C::GT - 1);
   const int b = jb.bh / p.H, h = jb.bh % p.H;
   const bf16* qg = (const bf16*)p.q + b * p.sqB + h * p.sqH;
   const bf16* kg = (const bf16*)p.k + b * p.skB + h * p.skH;
@@ -192,66 +232,65 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
   tv.seek(p, jb, 0, BN);
   if (!tv.valid(jb) && jb.epi == EPI_ACC && jb.acc_in) return;  // skipped pair
 
-  // staging: group A moves K tiles, group B moves V tiles (row-major, padded)
-  u32x4 stg[C::KC];
+  // staging: group A moves K tiles, group B moves V tiles, global memory to
+  // LDS directly.  Wave wg of a group loads blocks KC wg .. KC wg + KC-1 of a
+  // tile; lane l moves 16 bytes: row l / (D/8) of the block, column chunk
+  // l % (D/8).  Row offsets fit in 24-bit products (row strides are below
+  // 16 MiB, checked on the host).
   const bf16* ssrc = groupB ? vg : kg;
   const int64_t sstr = groupB ? p.svS : p.skS;
   const int soff = groupB ? C::K_TILE : 0;
-  const int srs = groupB ? VS : KS;
-  // This thread's chunks are rows srow0 + i * srstep of a tile, 16 bytes at
-  // column chunk scol8.  Their byte offsets from the tile's first row fit in
-  // 24-bit products (row strides are below 16 MiB, checked on the host), so a
-  // tile is loaded from one uniform base plus cheap per-thread offsets.
-  const int srow0 = gtid / (D / 8), scol8 = gtid % (D / 8);
-  constexpr int srstep = C::GT / (D / 8);
+  const int bstr = groupB ? C::VB : C::KB;
+  const int wg = wave & 3;
+  const int drow = lane / (D / 8), dcol = (lane % (D / 8)) * 16;
   const uint32_t sstr2 = (uint32_t)(sstr * 2);  // row stride in bytes, < 2^24
-  // Load the tile of `lim` keys (1..BN) starting at row0 of the staged tensor,
-  // branch-free: rows at or past lim repeat the last key (their scores are
-  // masked, their P is zero and the repeated V row is finite).
-  auto load_rows = [&](const bf16* row0, int lim) {
-    const char* base = (const char*)row0;
+  // Load the tile at key t.kt into LDS buffer buf, branch-free: rows at or
+  // past the segment end repeat its last key (their scores are masked, their
+  // P is zero and the repeated V row is finite).
+  auto dma_tile = [&](const TileIter& t, int buf) {
+    const int lim = (int)min(t.ke - t.kt, (int64_t)BN);
+    const char* base = (const char*)(ssrc + t.kt * sstr) + dcol;
 #pragma unroll
     for (int i = 0; i < C::KC; ++i) {
-      const int r = min(srow0 + i * srstep, lim - 1);
-      const uint32_t off = __umul24((uint32_t)r, sstr2) + (uint32_t)(scol8 * 16);
-      stg[i] = *(const u32x4*)(base + off);  // uniform base + 32-bit lane offset
+      const int blk = C::KC * wg + i;
+      const int r = min(blk * C::RPB + drow, lim - 1);
+      dma16(base + __umul24((uint32_t)r, sstr2), lds_addr(smem) + buf * C::STAGE + soff + blk * bstr);
     }
-  };
-  auto load_tile = [&](const TileIter& t) {
-    load_rows(ssrc + t.kt * sstr, (int)min(t.ke - t.kt, (int64_t)BN));
-  };
-  auto store_tile = [&](int buf) {
-    bf16* dst = smem + buf * C::STAGE + soff;
-#pragma unroll
-    for (int i = 0; i < C::KC; ++i)
-      *(u32x4*)(dst + (srow0 + i * srstep) * srs + scol8 * 8) = stg[i];
   };
 
   f32x16 sacc[BN / 32];
   bf16x8 pb[BN / 16];
+  // K operand of S^T = K Q^T: lane (lr, g) reads tile row kperm(u, lr),
+  // columns 16 s + 8 g ..
+  const int kbase = (lr % C::NBU) * C::KB + (lr / C::NBU) * C::ROWB + 16 * g;
   auto phase_s = [&](int buf) {
-    const bf16* ks = smem + buf * C::STAGE;
+    const char* ks = smem + buf * C::STAGE + kbase;
 #pragma unroll
     for (int u = 0; u < BN / 32; ++u) sacc[u] = f32x16{};
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
 #pragma unroll
       for (int u = 0; u < BN / 32; ++u) {
-        bf16x8 a = *(const bf16x8*)(ks + (32 * u + lr) * KS + 16 * s + 8 * g);
+        bf16x8 a = *(const bf16x8*)(ks + C::NBU * u * C::KB + 32 * s);
         sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], sacc[u], 0, 0, 0);
       }
   };
+  // V^T operand of O^T += V^T P^T: contraction position e of lane group g in
+  // step t = 2u + hh is S^T row m = 16 hh + 8 (e / 4) + 4 g + e % 4 of block
+  // pair u, i.e. tile row kperm(u, m); the 16 lanes of a transposing read
+  // address the four rows e % 4 = li / 4.
+  const int li = lane & 15, mm = 4 * g + (li >> 2);
+  const int vbase = C::K_TILE + (mm % C::NBU) * C::VB + (mm / C::NBU) * C::ROWB +
+                    32 * ((lane >> 4) & 1) + 8 * (li & 3);
   auto phase_pv = [&](int buf) {
-    const bf16* vt_s = smem + buf * C::STAGE + C::K_TILE;
-    const int li = lane & 15;
-    const bf16* vbase = vt_s + (li >> 2) * VS + ((lane >> 4) & 1) * 16 + 4 * (li & 3);
+    const char* vt_s = smem + buf * C::STAGE + vbase;
 #pragma unroll
     for (int t = 0; t < BN / 16; ++t)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const bf16* a0 = vbase + (16 * t + 4 * g) * VS + 32 * dt;
+        const char* a0 = vt_s + C::NBU * (t / 2) * C::VB + 512 * (t % 2) + 64 * dt;
         s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
-        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0 + 8 * VS));
+        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0 + 256));
         u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
         const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[t], oacc[dt], 0, 0, 0);
@@ -264,14 +303,17 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
       need_mask = __builtin_amdgcn_ballot_w64(
                       visible_prefix(t.kt, t.ke, 2, myrow, BN, p.blk, row_w, row_c) < BN) != 0;
     if (need_mask) {
-      const int lim = visible_prefix(t.kt, t.ke, p.causal, myrow, BN, p.blk, row_w, row_c);
+      // element 4i+jj of sacc[u] is S^T row m = 8i + 4g + jj, key kperm(u, m);
+      // the part of the key that depends on g is moved to the limit
+      const int gk = kperm<D>(0, 4 * g) - kperm<D>(0, 0);
+      const int lim = visible_prefix(t.kt, t.ke, p.causal, myrow, BN, p.blk, row_w, row_c) - gk;
 #pragma unroll
       for (int u = 0; u < BN / 32; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj)
-            if (32 * u + 8 * i + 4 * g + jj >= lim) sacc[u][4 * i + jj] = -INFINITY;
+            if (kperm<D>(u, 8 * i + jj) >= lim) sacc[u][4 * i + jj] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -310,20 +352,24 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
   // ---- prologue: tile 0 into buffer 0, tile 1 in flight.  A job without
   // visible tiles skips the prologue and the loop altogether (the condition is
   // uniform over the workgroup), so both groups always pass the same barriers.
-  TileIter tw = tv;  // next tile this thread's group stages
+  TileIter tw = tv;  // latest tile this thread's group has loaded
   if (tv.valid(jb)) {
-    load_tile(tw);
-    store_tile(0);
+    dma_tile(tw, 0);
     tw.advance(p, jb, BN);
-    if (tw.valid(jb)) load_tile(tw);
-    __syncthreads();
+    if (tw.valid(jb)) {
+      dma_tile(tw, 1);
+      wait_vm<C::KC>();  // tile 0 has landed, tile 1 is in flight
+    } else {
+      wait_vm<0>();
+    }
+    slot_barrier();
     if (!groupB) {
       phase_s(0);  // slot 0
-      __syncthreads();
+      slot_barrier();
     } else {
-      __syncthreads();  // slot 0: idle
-      phase_s(0);       // slot 1
-      __syncthreads();
+      slot_barrier();  // slot 0: idle
+      phase_s(0);      // slot 1
+      slot_barrier();
     }
     // Settle the prologue's global loads (Q, the carried accumulator) here: the
     // wait-count pass cannot tell that the loop's first MFMAs already waited for
@@ -339,12 +385,12 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int t = 0; t < BN / 16; ++t) pin(pb[t]);
       pin(lsum);
-      if (tw.valid(jb)) {  // stage tile j+1, fetch tile j+2
-        store_tile(nxt);
+      if (tw.valid(jb)) {  // tile j+1 has landed (published by the barrier below); load tile j+2
+        wait_vm<0>();
         tw.advance(p, jb, BN);
-        if (tw.valid(jb)) load_tile(tw);
+        if (tw.valid(jb)) dma_tile(tw, (j + 2) % 3);
       }
-      __syncthreads();
+      slot_barrier();
       TileIter tn = tv;
       tn.advance(p, jb, BN);
       phase_pv(cur);
@@ -352,7 +398,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int u = 0; u < BN / 32; ++u) pin(sacc[u]);
       // group A closes this slot; group B's last MFMA slot is the final one
-      if (!groupB || tn.valid(jb)) __syncthreads();
+      if (!groupB || tn.valid(jb)) slot_barrier();
       tv = tn;
       ++j;
     }
