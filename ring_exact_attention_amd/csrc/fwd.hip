@@ -154,15 +154,15 @@ __device__ constexpr int kperm(int u, int m) {
 // stay in flight across it (their completion is awaited explicitly before the
 // barrier that publishes them); this wave's LDS reads are complete first.
 __device__ inline void slot_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// One direct global->LDS load: 16 bytes per lane from gaddr to LDS byte
-// address lds + 16 * lane (lds wave-uniform, passed in m0).  Issued from asm
-// so that the compiler adds no waits of its own for it; every read of the
-// loaded data follows an explicit wait_vm and a barrier.  Nothing else in the
-// kernel keeps a value in m0.
+// One direct global->LDS load: 16 bytes per lane from base + off to LDS byte
+// address lds + 16 * lane (base and lds wave-uniform; lds passed in m0).
+// Issued from asm so that the compiler adds no waits of its own for it; every
+// read of the loaded data follows an explicit wait_vm and a barrier.  Nothing
+// else in the kernel keeps a value in m0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved: the asm sets it itself
-__device__ inline void dma16(const void* gaddr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds)
+__device__ inline void dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -244,17 +244,27 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
   const int wg = wave & 3;
   const int drow = lane / (D / 8), dcol = (lane % (D / 8)) * 16;
   const uint32_t sstr2 = (uint32_t)(sstr * 2);  // row stride in bytes, < 2^24
-  // Load the tile at key t.kt into LDS buffer buf, branch-free: rows at or
-  // past the segment end repeat its last key (their scores are masked, their
-  // P is zero and the repeated V row is finite).
+  // the lane's byte offsets from a tile's first row, one per block it loads
+  uint32_t doff[C::KC];
+#pragma unroll
+  for (int i = 0; i < C::KC; ++i)
+    doff[i] = __umul24((uint32_t)((C::KC * wg + i) * C::RPB + drow), sstr2) + (uint32_t)dcol;
+  // Load the tile at key t.kt into LDS buffer buf.  In a tile that ends
+  // early, rows at or past the segment end repeat its last key (their scores
+  // are masked, their P is zero and the repeated V row is finite).
   auto dma_tile = [&](const TileIter& t, int buf) {
     const int lim = (int)min(t.ke - t.kt, (int64_t)BN);
-    const char* base = (const char*)(ssrc + t.kt * sstr) + dcol;
+    const bf16* base = ssrc + t.kt * sstr;
+    const uint32_t lds = lds_addr(smem) + buf * C::STAGE + soff + C::KC * wg * bstr;
+    if (lim == BN) {
 #pragma unroll
-    for (int i = 0; i < C::KC; ++i) {
-      const int blk = C::KC * wg + i;
-      const int r = min(blk * C::RPB + drow, lim - 1);
-      dma16(base + __umul24((uint32_t)r, sstr2), lds_addr(smem) + buf * C::STAGE + soff + blk * bstr);
+      for (int i = 0; i < C::KC; ++i) dma16(base, doff[i], lds + i * bstr);
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::KC; ++i) {
+        const int r = min((C::KC * wg + i) * C::RPB + drow, lim - 1);
+        dma16(base, __umul24((uint32_t)r, sstr2) + (uint32_t)dcol, lds + i * bstr);
+      }
     }
   };
 
