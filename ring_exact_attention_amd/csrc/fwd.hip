@@ -18,11 +18,13 @@
 // with ds_read_b64_tr_b16, which hands each lane one column of a 4-row block
 // (four keys of one head dim).
 //
-// The running maximum is only moved when some row's maximum grows by more
-// than 2^8 (log2 units): until then probabilities are taken relative to the
-// stale maximum (they stay <= 256, exact in fp32 and bf16 range), and the
-// O accumulator is not rescaled.  Output and LSE are unchanged by this: O and
-// l always share one reference maximum.
+// The running maximum (the reference P is taken relative to) is only moved
+// when some row's maximum grows by more than 8 (log2 units): until then
+// probabilities are taken relative to the stale maximum and the O
+// accumulator is not rescaled.  A tile's maximum is not even computed unless
+// some lane's sum of P over the tile exceeds 2^16, so a P can reach 2^16
+// (well inside fp32 and bf16 range).  Output and LSE are unchanged by this:
+// O and l always share one reference.
 //
 // fp32 kernel: plain VALU arithmetic (fp32 products and sums), four lanes per
 // query row; used for fp32 inputs where fp32-exact products are required.
@@ -82,6 +84,11 @@ __device__ inline void pin(T& x) {
 
 // Growth of a row maximum (log2 units) tolerated before the O accumulator is rescaled.
 constexpr float kLazyRescale = 8.f;
+// Largest sum of one lane's P over a tile (relative to the row's reference)
+// accepted without looking at the tile's maximum.  Beyond it some P exceeds
+// 2^11, so the maximum has grown by more than kLazyRescale and the reference
+// is moved.
+constexpr float kFastGrowth = 65536.f;
 
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
   bf16 x = (bf16)a, y = (bf16)b;  // round to nearest even (v_cvt_pk_bf16_f32)
@@ -325,38 +332,55 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
           for (int jj = 0; jj < 4; ++jj)
             if (kperm<D>(u, 8 * i + jj) >= lim) sacc[u][4 * i + jj] = -INFINITY;
     }
-    float mx = -INFINITY;
+    // P of the tile relative to reference m (log2 units) into pb; returns
+    // this lane's sum of it
+    auto exp_tile = [&](float m) -> float {
+      float ts[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < BN / 32; ++u)
+      for (int u = 0; u < BN / 32; ++u)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[u][e]);
-    mx = wave_swap32_max(mx);
-    const float m_cand = fmaxf(m2, mx * c2);
-    if (__builtin_amdgcn_ballot_w64(m_cand > m2 + kLazyRescale) != 0) {
-      const float alpha = fast_exp2(m2 - ((m_cand == -INFINITY) ? 0.f : m_cand));
-      lsum *= alpha;
+        for (int hh = 0; hh < 2; ++hh) {
+          bf16x8 x;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
-      m2 = m_cand;
-    }
-    const float m_use = (m2 == -INFINITY) ? 0.f : m2;
-    float ts[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < BN / 32; ++u)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        bf16x8 x;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float pv = fast_exp2(__builtin_fmaf(sacc[u][8 * hh + e], c2, -m_use));
-          ts[e & 3] += pv;
-          x[e] = (bf16)pv;
+          for (int e = 0; e < 8; ++e) {
+            float pv = fast_exp2(__builtin_fmaf(sacc[u][8 * hh + e], c2, -m));
+            ts[e & 3] += pv;
+            x[e] = (bf16)pv;
+          }
+          pb[2 * u + hh] = x;
         }
-        pb[2 * u + hh] = x;
+      return (ts[0] + ts[1]) + (ts[2] + ts[3]);
+    };
+    // Common case: every row of the wave has a reference and no P of this
+    // tile exceeds kFastGrowth (checked through the lane's sum of P), so the
+    // tile's maximum is not needed.  Otherwise the maximum is taken, the
+    // reference moved if it grew by more than kLazyRescale, and P recomputed.
+    bool slow = __builtin_amdgcn_ballot_w64(m2 == -INFINITY) != 0;
+    float tsum = 0.f;
+    if (!slow) {
+      tsum = exp_tile(m2);
+      slow = __builtin_amdgcn_ballot_w64(!(tsum <= kFastGrowth)) != 0;
+    }
+    if (slow) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < BN / 32; ++u)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[u][e]);
+      mx = wave_swap32_max(mx);
+      const float m_cand = fmaxf(m2, mx * c2);
+      if (__builtin_amdgcn_ballot_w64(m_cand > m2 + kLazyRescale) != 0) {
+        const float alpha = fast_exp2(m2 - ((m_cand == -INFINITY) ? 0.f : m_cand));
+        lsum *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+        m2 = m_cand;
       }
-    lsum += (ts[0] + ts[1]) + (ts[2] + ts[3]);
+      tsum = exp_tile((m2 == -INFINITY) ? 0.f : m2);
+    }
+    lsum += tsum;
   };
 
   // ---- prologue: tile 0 into buffer 0, tile 1 in flight.  A job without
