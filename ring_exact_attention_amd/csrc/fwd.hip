@@ -8,15 +8,19 @@
 // ("What carries the argument"); seeding the state from an incoming
 // (O_prev, LSE_prev) continues that merge inside the kernel.
 //
-// bf16 kernel: both contractions run on v_mfma_f32_32x32x16_bf16.  Each wave
-// owns 32 query rows and computes S^T = K Q^T (keys x queries) so that every
-// lane holds one query's scores: row max / sum are in-lane reductions plus one
-// exchange with lane l^32.  The PV product is O^T = V^T P^T, whose B operand
-// is exactly the lane's own scores converted to bf16, and whose accumulator
-// rows are rescaled by the lane's own factor.  V^T needs keys contiguous in
-// the A operand: V tiles are staged row-major like K, and the operand is read
-// with ds_read_b64_tr_b16, which hands each lane one column of a 4-row block
-// (four keys of one head dim).
+// bf16 kernel: both contractions run on v_mfma_f32_16x16x32_bf16 (rather
+// than 32x32x16: per FLOP it moves half the accumulator data through the
+// register file, which the chip's power limit and the VALU work of the other
+// wave on the SIMD both reward).  Each wave owns 32 query rows as two 16-row
+// blocks and computes S^T = K Q^T (keys x queries), so that every lane holds
+// scores of two query rows, 16 keys of each per 64-key tile; a row's other
+// keys sit in three other lanes (a row max or sum takes two lane exchanges).
+// The PV product is O^T = V^T P^T, whose B operand is the lane's own scores
+// converted to bf16, and whose accumulator rows are rescaled by the lane's
+// own factors.  V^T needs keys contiguous in the A operand: V tiles are
+// staged row-major like K, and the operand is read with ds_read_b64_tr_b16,
+// which hands each lane one column of a 4-row block (four keys of one head
+// dim).
 //
 // The running maximum (the reference P is taken relative to) is only moved
 // when some row's maximum grows by more than 8 (log2 units): until then
@@ -44,6 +48,17 @@ __device__ inline float wave_swap32_max(float x) {
 
 __device__ inline float wave_swap32_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// v_permlane16_swap does the same for lane l and lane l^16.
+__device__ inline float wave_swap16_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ inline float wave_swap16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
@@ -114,8 +129,8 @@ __device__ inline void store4<bf16>(bf16* dst, float a, float b, float c, float 
 // of tile j+1) and a VALU phase (mask, max, exp2, row sums and the bf16 P of
 // tile j+1).  Waves 0-3 (group A) and 4-7 (group B) share the four SIMDs one
 // each and run one phase apart: between any two barriers one wave of every
-// SIMD is in its MFMA phase while the other is in its VALU phase, so the
-// matrix core and the vector ALU work at the same time.  Barrier intervals
+// SIMD is in its MFMA phase while the other is in its VALU phase, so that
+// the matrix core and the vector ALU can work at the same time.  Barrier intervals
 // ("slots") are numbered from 0; group A runs
 //   slot 0: S(0);  slot 2j+1: softmax(j), load K(j+2);  slot 2j+2: PV(j) + S(j+1)
 // and group B runs the same sequence one slot later (loading V(j+2) in its
@@ -132,29 +147,27 @@ struct Bf16Fwd {
   static constexpr int D = D_, NW = 8, NT = 512, BM = 256, BN = 64;
   // K and V tiles go from global memory straight to LDS, one 1 KB block (RPB
   // rows of ROWB bytes) per wave and load instruction, so rows are unpadded
-  // inside a block and blocks are padded: K blocks by 32 bytes, V blocks by
-  // 64 (byte strides KB, VB).  Key order in a tile is permuted (kperm below)
-  // so that both read patterns are free of bank conflicts:
-  //   K, ds_read_b128, eight lanes at a time: lanes 0-7 read eight blocks,
-  //     32 bytes apart in the bank space;
-  //   V, ds_read_b64_tr_b16, 32 lanes at a time over 4 rows x 64 bytes: the
-  //     four rows lie in four blocks, 64 bytes apart in the bank space.
-  static constexpr int ROWB = 2 * D, RPB = 1024 / ROWB, NBK = BN / RPB, NBU = NBK / 2;
-  static constexpr int KB = 1024 + 32, VB = 1024 + 64;
-  static constexpr int K_TILE = NBK * KB, V_TILE = NBK * VB;  // bytes
+  // inside a block and blocks are padded by 32 bytes (byte stride BS).  Key
+  // order in a tile is permuted (kperm below) so that the eight rows read
+  // together lie in eight blocks, 32 bytes apart in the bank space: K by
+  // ds_read_b128 (eight lanes at a time, one row each), V by
+  // ds_read_b64_tr_b16 (32 lanes at a time over 8 rows x 32 bytes).
+  static constexpr int ROWB = 2 * D, RPB = 1024 / ROWB, NBK = BN / RPB, NBH = NBK / 2;
+  static constexpr int BS = 1024 + 32;
+  static constexpr int K_TILE = NBK * BS, V_TILE = NBK * BS;  // bytes
   static constexpr int STAGE = K_TILE + V_TILE;
   static constexpr int NBUF = 3;
-  static constexpr int GT = NT / 2;  // threads per group
   static constexpr int KC = NBK / 4;  // blocks per wave and tile (four waves per group)
-  static_assert(RPB * NBU == 32 && KC * 4 == NBK, "tile geometry");
+  static_assert(NBH * RPB == 32 && KC * 4 == NBK && NBH >= 4, "tile geometry");
 };
 
-// Tile row (key offset) held by row m of block pair u of the MFMA operands:
-// storage block (m mod NBU) + NBU u, row m / NBU of that block.
+// Storage of row m (0..15) of 16-key block kb (0..3) of a tile: block
+// (m mod NBH) + NBH (kb mod 2), row m / NBH + (16 / NBH) (kb / 2); kperm is its
+// key offset in the tile (RPB rows per block, in order).
 template <int D>
-__device__ constexpr int kperm(int u, int m) {
+__device__ constexpr int kperm(int kb, int m) {
   using C = Bf16Fwd<D>;
-  return C::RPB * (m % C::NBU) + 32 * u + m / C::NBU;
+  return C::RPB * (m % C::NBH + C::NBH * (kb % 2)) + m / C::NBH + (16 / C::NBH) * (kb / 2);
 }
 
 // Barrier without the memory fence of __syncthreads: direct-to-LDS loads
@@ -186,7 +199,7 @@ __device__ inline void wait_vm() {
 template <int D_>
 __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
   using C = Bf16Fwd<D_>;
-  constexpr int D = C::D, BN = C::BN;
+  constexpr int D = C::D, BN = C::BN, NKB = BN / 16, NKK = BN / 32, NKS = D / 32, NDB = D / 16;
   __shared__ __attribute__((aligned(16))) char smem[C::NBUF * C::STAGE];
 
   Job jb;
@@ -195,8 +208,13 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
-  const int lr = lane & 31;
-  const int g = lane >> 5;
+  // Lane layout of the 16x16x32 blocks: lane l has column l16 = l % 16 and
+  // quarter q4 = l / 16.  A wave's 32 query rows are two 16-row blocks qb; the
+  // lane owns row wrow0 + 16 qb + l16 of each.  A score block (16 keys x 16
+  // rows) gives the lane rows 4 q4 + r (r = 0..3) of key block kb, keys
+  // kperm(kb, 4 q4 + r); the row's other keys sit in lanes l16 + 16 q.
+  const int l16 = lane & 15;
+  const int q4 = lane >> 4;
   const bool groupB = wave >= 4;
   const int b = jb.bh / p.H, h = jb.bh % p.H;
   const bf16* qg = (const bf16*)p.q + b * p.sqB + h * p.sqH;
@@ -204,34 +222,41 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
   const bf16* vg = (const bf16*)p.v + b * p.svB + h * p.svH;
 
   const int64_t wrow0 = jb.r0 + wave * 32;
-  const int64_t myrow = wrow0 + lr;
-  const bool row_ok = myrow < jb.r1;
-  const int64_t row_w = p.causal == 2 ? myrow / p.blk : 0;  // striped: shard, index
-  const int64_t row_c = p.causal == 2 ? myrow - row_w * p.blk : 0;
-  bf16x8 qreg[D / 16];
+  int64_t myrow[2], row_w[2], row_c[2];
+  bool row_ok[2];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s)
-    qreg[s] = row_ok ? *(const bf16x8*)(qg + myrow * p.sqS + 16 * s + 8 * g) : bf16x8{};
+  for (int qb = 0; qb < 2; ++qb) {
+    myrow[qb] = wrow0 + 16 * qb + l16;
+    row_ok[qb] = myrow[qb] < jb.r1;
+    row_w[qb] = p.causal == 2 ? myrow[qb] / p.blk : 0;  // striped: shard, index
+    row_c[qb] = p.causal == 2 ? myrow[qb] - row_w[qb] * p.blk : 0;
+  }
+  // B operand of S^T = K Q^T: Q row 16 qb + l16, head dims 32 ks + 8 q4 ..
+  bf16x8 qreg[2][NKS];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      qreg[qb][ks] = row_ok[qb] ? *(const bf16x8*)(qg + myrow[qb] * p.sqS + 32 * ks + 8 * q4) : bf16x8{};
 
-  float m2 = -INFINITY, lsum = 0.f;
-  f32x16 oacc[D / 32];
+  // O^T blocks (16 head dims x 16 rows): the lane holds dims 16 db + 4 q4 + r
+  // of its row of block qb
+  float m2[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+  f32x4 oacc[NDB][2];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
+  for (int db = 0; db < NDB; ++db) oacc[db][0] = oacc[db][1] = f32x4{};
   const int64_t BH = (int64_t)p.B * p.H;
   if (jb.epi == EPI_ACC && jb.acc_in) {
-    float lp = row_ok ? p.lse[jb.bh * p.SQ + myrow] : -INFINITY;
-    if (lp != -INFINITY) {
-      m2 = lp * kLog2e;
-      lsum = (g == 0) ? 1.f : 0.f;
-      const float* src = p.o_acc + (jb.bh * p.SQ + myrow) * D;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+    for (int qb = 0; qb < 2; ++qb) {
+      const float lp = row_ok[qb] ? p.lse[jb.bh * p.SQ + myrow[qb]] : -INFINITY;
+      if (lp != -INFINITY) {
+        m2[qb] = lp * kLog2e;
+        lsum[qb] = (q4 == 0) ? 1.f : 0.f;
+        const float* src = p.o_acc + (jb.bh * p.SQ + myrow[qb]) * D + 4 * q4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f32x4 x = *(const f32x4*)(src + 32 * dt + 8 * i + 4 * g);
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) oacc[dt][4 * i + jj] = x[jj];
-        }
+        for (int db = 0; db < NDB; ++db) oacc[db][qb] = *(const f32x4*)(src + 16 * db);
+      }
     }
   }
 
@@ -247,7 +272,6 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
   const bf16* ssrc = groupB ? vg : kg;
   const int64_t sstr = groupB ? p.svS : p.skS;
   const int soff = groupB ? C::K_TILE : 0;
-  const int bstr = groupB ? C::VB : C::KB;
   const int wg = wave & 3;
   const int drow = lane / (D / 8), dcol = (lane % (D / 8)) * 16;
   const uint32_t sstr2 = (uint32_t)(sstr * 2);  // row stride in bytes, < 2^24
@@ -262,55 +286,62 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
   auto dma_tile = [&](const TileIter& t, int buf) {
     const int lim = (int)min(t.ke - t.kt, (int64_t)BN);
     const bf16* base = ssrc + t.kt * sstr;
-    const uint32_t lds = lds_addr(smem) + buf * C::STAGE + soff + C::KC * wg * bstr;
+    const uint32_t lds = lds_addr(smem) + buf * C::STAGE + soff + C::KC * wg * C::BS;
     if (lim == BN) {
 #pragma unroll
-      for (int i = 0; i < C::KC; ++i) dma16(base, doff[i], lds + i * bstr);
+      for (int i = 0; i < C::KC; ++i) dma16(base, doff[i], lds + i * C::BS);
     } else {
 #pragma unroll
       for (int i = 0; i < C::KC; ++i) {
         const int r = min((C::KC * wg + i) * C::RPB + drow, lim - 1);
-        dma16(base, __umul24((uint32_t)r, sstr2) + (uint32_t)dcol, lds + i * bstr);
+        dma16(base, __umul24((uint32_t)r, sstr2) + (uint32_t)dcol, lds + i * C::BS);
       }
     }
   };
 
-  f32x16 sacc[BN / 32];
-  bf16x8 pb[BN / 16];
-  // K operand of S^T = K Q^T: lane (lr, g) reads tile row kperm(u, lr),
-  // columns 16 s + 8 g ..
-  const int kbase = (lr % C::NBU) * C::KB + (lr / C::NBU) * C::ROWB + 16 * g;
+  // Scores of the tile: sacc[kb][qb] element r is key kperm(kb, 4 q4 + r) of
+  // the lane's row in block qb.  PV contracts over 32 keys per MFMA; its k
+  // positions 8 q4 + (0..3) and 8 q4 + (4..7) are taken as the keys of
+  // blocks 2 kk and 2 kk + 1 that the lane holds, so that the B operand P^T
+  // is the lane's own scores, and V^T is read in the same order.
+  f32x4 sacc[NKB][2];
+  bf16x8 pb[NKK][2];
+  // K operand: lane (l16, q4) reads row l16 of key block kb, columns 32 ks + 8 q4 ..
+  const int kbase = (l16 % C::NBH) * C::BS + (l16 / C::NBH) * C::ROWB + 16 * q4;
   auto phase_s = [&](int buf) {
-    const char* ks = smem + buf * C::STAGE + kbase;
+    const char* ks_ = smem + buf * C::STAGE + kbase;
 #pragma unroll
-    for (int u = 0; u < BN / 32; ++u) sacc[u] = f32x16{};
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s)
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 a = *(const bf16x8*)(ks_ + C::NBH * (kb % 2) * C::BS +
+                                          (16 / C::NBH) * (kb / 2) * C::ROWB + 64 * ks);
 #pragma unroll
-      for (int u = 0; u < BN / 32; ++u) {
-        bf16x8 a = *(const bf16x8*)(ks + C::NBU * u * C::KB + 32 * s);
-        sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], sacc[u], 0, 0, 0);
+        for (int qb = 0; qb < 2; ++qb)
+          sacc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              a, qreg[qb][ks], ks == 0 ? f32x4{} : sacc[kb][qb], 0, 0, 0);
       }
   };
-  // V^T operand of O^T += V^T P^T: contraction position e of lane group g in
-  // step t = 2u + hh is S^T row m = 16 hh + 8 (e / 4) + 4 g + e % 4 of block
-  // pair u, i.e. tile row kperm(u, m); the 16 lanes of a transposing read
-  // address the four rows e % 4 = li / 4.
-  const int li = lane & 15, mm = 4 * g + (li >> 2);
-  const int vbase = C::K_TILE + (mm % C::NBU) * C::VB + (mm / C::NBU) * C::ROWB +
-                    32 * ((lane >> 4) & 1) + 8 * (li & 3);
+  // V^T operand of key half kk and head-dim block db: a transposing read
+  // hands lane l16 of quarter q4 head dim 16 db + l16 of rows 4 q4 + (0..3) of
+  // key block 2 kk (lo) and 2 kk + 1 (hi); the 16 lanes address the four rows
+  // li / 4 (li = l16), columns 4 (li % 4).
+  const int vm = 4 * q4 + (l16 >> 2);
+  const int vbase = C::K_TILE + (vm % C::NBH) * C::BS + (vm / C::NBH) * C::ROWB + 8 * (l16 & 3);
   auto phase_pv = [&](int buf) {
     const char* vt_s = smem + buf * C::STAGE + vbase;
 #pragma unroll
-    for (int t = 0; t < BN / 16; ++t)
+    for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const char* a0 = vt_s + C::NBU * (t / 2) * C::VB + 512 * (t % 2) + 64 * dt;
+      for (int db = 0; db < NDB; ++db) {
+        const char* a0 = vt_s + (16 / C::NBH) * kk * C::ROWB + 32 * db;
         s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
-        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0 + 256));
+        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0 + C::NBH * C::BS));
         u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
         const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[t], oacc[dt], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[kk][qb], oacc[db][qb], 0, 0, 0);
       }
   };
   const float c2 = p.scale_log2;
@@ -318,69 +349,81 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     bool need_mask = (t.kt + BN > t.ke) || (p.causal == 1 && t.kt + BN - 1 > wrow0);
     if (p.causal == 2)
       need_mask = __builtin_amdgcn_ballot_w64(
-                      visible_prefix(t.kt, t.ke, 2, myrow, BN, p.blk, row_w, row_c) < BN) != 0;
+                      visible_prefix(t.kt, t.ke, 2, myrow[0], BN, p.blk, row_w[0], row_c[0]) < BN ||
+                      visible_prefix(t.kt, t.ke, 2, myrow[1], BN, p.blk, row_w[1], row_c[1]) < BN) != 0;
     if (need_mask) {
-      // element 4i+jj of sacc[u] is S^T row m = 8i + 4g + jj, key kperm(u, m);
-      // the part of the key that depends on g is moved to the limit
-      const int gk = kperm<D>(0, 4 * g) - kperm<D>(0, 0);
-      const int lim = visible_prefix(t.kt, t.ke, p.causal, myrow, BN, p.blk, row_w, row_c) - gk;
+      // the part of the key that depends on q4 is moved to the limit
+      const int gk = kperm<D>(0, 4 * q4) - kperm<D>(0, 0);
 #pragma unroll
-      for (int u = 0; u < BN / 32; ++u)
+      for (int qb = 0; qb < 2; ++qb) {
+        const int lim =
+            visible_prefix(t.kt, t.ke, p.causal, myrow[qb], BN, p.blk, row_w[qb], row_c[qb]) - gk;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-            if (kperm<D>(u, 8 * i + jj) >= lim) sacc[u][4 * i + jj] = -INFINITY;
+          for (int r = 0; r < 4; ++r)
+            if (kperm<D>(kb, r) >= lim) sacc[kb][qb][r] = -INFINITY;
+      }
     }
-    // P of the tile relative to reference m (log2 units) into pb; returns
-    // this lane's sum of it
-    auto exp_tile = [&](float m) -> float {
-      float ts[4] = {0.f, 0.f, 0.f, 0.f};
+    // P relative to references m[qb] (log2 units) into pb; ts[qb] is this
+    // lane's sum of it
+    auto exp_tile = [&](const float* m, float* ts) {
 #pragma unroll
-      for (int u = 0; u < BN / 32; ++u)
+      for (int qb = 0; qb < 2; ++qb) {
+        float s2[2] = {0.f, 0.f};
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
+        for (int kk = 0; kk < NKK; ++kk) {
           bf16x8 x;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            float pv = fast_exp2(__builtin_fmaf(sacc[u][8 * hh + e], c2, -m));
-            ts[e & 3] += pv;
+            const float pv = fast_exp2(__builtin_fmaf(sacc[2 * kk + e / 4][qb][e % 4], c2, -m[qb]));
+            s2[e & 1] += pv;
             x[e] = (bf16)pv;
           }
-          pb[2 * u + hh] = x;
+          pb[kk][qb] = x;
         }
-      return (ts[0] + ts[1]) + (ts[2] + ts[3]);
+        ts[qb] = s2[0] + s2[1];
+      }
     };
     // Common case: every row of the wave has a reference and no P of this
-    // tile exceeds kFastGrowth (checked through the lane's sum of P), so the
+    // tile exceeds kFastGrowth (checked through the lane's sums of P), so the
     // tile's maximum is not needed.  Otherwise the maximum is taken, the
     // reference moved if it grew by more than kLazyRescale, and P recomputed.
-    bool slow = __builtin_amdgcn_ballot_w64(m2 == -INFINITY) != 0;
-    float tsum = 0.f;
+    bool slow = __builtin_amdgcn_ballot_w64(m2[0] == -INFINITY || m2[1] == -INFINITY) != 0;
+    float ts[2] = {0.f, 0.f};
     if (!slow) {
-      tsum = exp_tile(m2);
-      slow = __builtin_amdgcn_ballot_w64(!(tsum <= kFastGrowth)) != 0;
+      exp_tile(m2, ts);
+      slow = __builtin_amdgcn_ballot_w64(!(ts[0] <= kFastGrowth) || !(ts[1] <= kFastGrowth)) != 0;
     }
     if (slow) {
-      float mx = -INFINITY;
+      float m_cand[2];
+      bool grow = false;
 #pragma unroll
-      for (int u = 0; u < BN / 32; ++u)
+      for (int qb = 0; qb < 2; ++qb) {
+        float mx = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[u][e]);
-      mx = wave_swap32_max(mx);
-      const float m_cand = fmaxf(m2, mx * c2);
-      if (__builtin_amdgcn_ballot_w64(m_cand > m2 + kLazyRescale) != 0) {
-        const float alpha = fast_exp2(m2 - ((m_cand == -INFINITY) ? 0.f : m_cand));
-        lsum *= alpha;
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
-        m2 = m_cand;
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kb][qb][r]);
+        mx = wave_swap32_max(wave_swap16_max(mx));
+        m_cand[qb] = fmaxf(m2[qb], mx * c2);
+        grow = grow || (m_cand[qb] > m2[qb] + kLazyRescale);
       }
-      tsum = exp_tile((m2 == -INFINITY) ? 0.f : m2);
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const float alpha = fast_exp2(m2[qb] - ((m_cand[qb] == -INFINITY) ? 0.f : m_cand[qb]));
+          lsum[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) oacc[db][qb] *= alpha;
+          m2[qb] = m_cand[qb];
+        }
+      }
+      const float m_use[2] = {(m2[0] == -INFINITY) ? 0.f : m2[0], (m2[1] == -INFINITY) ? 0.f : m2[1]};
+      exp_tile(m_use, ts);
     }
-    lsum += tsum;
+    lsum[0] += ts[0];
+    lsum[1] += ts[1];
   };
 
   // ---- prologue: tile 0 into buffer 0, tile 1 in flight.  A job without
@@ -409,16 +452,26 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     // wait-count pass cannot tell that the loop's first MFMAs already waited for
     // them, and would otherwise wait on every tile's staging loads as well.
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) pin(qreg[s]);
+    for (int ks = 0; ks < NKS; ++ks) {
+      pin(qreg[0][ks]);
+      pin(qreg[1][ks]);
+    }
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) pin(oacc[dt]);
+    for (int db = 0; db < NDB; ++db) {
+      pin(oacc[db][0]);
+      pin(oacc[db][1]);
+    }
     int j = 0;
     while (tv.valid(jb)) {
       const int cur = j % 3, nxt = (j + 1) % 3;
       phase_softmax(tv);
 #pragma unroll
-      for (int t = 0; t < BN / 16; ++t) pin(pb[t]);
-      pin(lsum);
+      for (int kk = 0; kk < NKK; ++kk) {
+        pin(pb[kk][0]);
+        pin(pb[kk][1]);
+      }
+      pin(lsum[0]);
+      pin(lsum[1]);
       if (tw.valid(jb)) {  // tile j+1 has landed (published by the barrier below); load tile j+2
         wait_vm<0>();
         tw.advance(p, jb, BN);
@@ -430,7 +483,10 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
       phase_pv(cur);
       if (tn.valid(jb)) phase_s(nxt);
 #pragma unroll
-      for (int u = 0; u < BN / 32; ++u) pin(sacc[u]);
+      for (int kb = 0; kb < NKB; ++kb) {
+        pin(sacc[kb][0]);
+        pin(sacc[kb][1]);
+      }
       // group A closes this slot; group B's last MFMA slot is the final one
       if (!groupB || tn.valid(jb)) slot_barrier();
       tv = tn;
@@ -438,38 +494,35 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     }
   }  // tv.valid(jb)
 
-  // ---- epilogue
-  const float ltot = wave_swap32_sum(lsum);
-  const bool empty = (m2 == -INFINITY) || !(ltot > 0.f);
-  const float inv = empty ? 0.f : 1.f / ltot;
-  const float lse = empty ? -INFINITY : (m2 + __log2f(ltot)) * kLn2;
-  if (!row_ok) return;
-  if (jb.epi == EPI_FINAL) {
-    bf16* dst = (bf16*)p.o + b * p.soB + h * p.soH + myrow * p.soS;
+  // ---- epilogue: a row's sum is spread over the four lanes of its column
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+  for (int qb = 0; qb < 2; ++qb) {
+    const float ltot = wave_swap32_sum(wave_swap16_sum(lsum[qb]));
+    const bool empty = (m2[qb] == -INFINITY) || !(ltot > 0.f);
+    const float inv = empty ? 0.f : 1.f / ltot;
+    const float lse = empty ? -INFINITY : (m2[qb] + __log2f(ltot)) * kLn2;
+    if (!row_ok[qb]) continue;
+    if (jb.epi == EPI_FINAL) {
+      bf16* dst = (bf16*)p.o + b * p.soB + h * p.soH + myrow[qb] * p.soS + 4 * q4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        store4<bf16>(dst + 32 * dt + 8 * i + 4 * g, oacc[dt][4 * i] * inv,
-                     oacc[dt][4 * i + 1] * inv, oacc[dt][4 * i + 2] * inv,
-                     oacc[dt][4 * i + 3] * inv);
-    if (g == 0) p.lse[jb.bh * p.SQ + myrow] = lse;
-  } else {
-    float* obase = p.o_acc;
-    float* lbase = p.lse;
-    if (jb.epi == EPI_PART) {
-      obase += (int64_t)jb.block * BH * p.SQ * D;
-      lbase = p.lse_part + (int64_t)jb.block * BH * p.SQ;
+      for (int db = 0; db < NDB; ++db)
+        store4<bf16>(dst + 16 * db, oacc[db][qb][0] * inv, oacc[db][qb][1] * inv,
+                     oacc[db][qb][2] * inv, oacc[db][qb][3] * inv);
+      if (q4 == 0) p.lse[jb.bh * p.SQ + myrow[qb]] = lse;
+    } else {
+      float* obase = p.o_acc;
+      float* lbase = p.lse;
+      if (jb.epi == EPI_PART) {
+        obase += (int64_t)jb.block * BH * p.SQ * D;
+        lbase = p.lse_part + (int64_t)jb.block * BH * p.SQ;
+      }
+      float* dst = obase + (jb.bh * p.SQ + myrow[qb]) * D + 4 * q4;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        store4<float>(dst + 16 * db, oacc[db][qb][0] * inv, oacc[db][qb][1] * inv,
+                      oacc[db][qb][2] * inv, oacc[db][qb][3] * inv);
+      if (q4 == 0) lbase[jb.bh * p.SQ + myrow[qb]] = lse;
     }
-    float* dst = obase + (jb.bh * p.SQ + myrow) * D;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        store4<float>(dst + 32 * dt + 8 * i + 4 * g, oacc[dt][4 * i] * inv,
-                      oacc[dt][4 * i + 1] * inv, oacc[dt][4 * i + 2] * inv,
-                      oacc[dt][4 * i + 3] * inv);
-    if (g == 0) lbase[jb.bh * p.SQ + myrow] = lse;
   }
 }
 
