@@ -362,26 +362,41 @@ def summarize_pmc(pmc_dir: str, bench_log: str, name: str, tag: str, command: st
         avg = {c: sum(x[1].get(c, 0.0) for x in timed) / len(timed) for c in counters}
         lines.append(f"{_short(k)}: {dur / 1e3:.1f} us")
         lines.append("    " + "  ".join(f"{c}={v:.4g}" for c, v in avg.items()))
+        # a counter that reads a nonzero multiple of 2^24 in any timed dispatch
+        # has hit its limit (a natural count is such a multiple one time in 2^24)
+        clamped = sorted(c for c in counters if any(_clamped(x[1].get(c, 0.0)) for x in timed))
+        if clamped:
+            lines.append("    clamped (multiple of 2^24, not a count): " + " ".join(clamped))
+
+        def ratio(label, num, den, fmt):
+            if avg.get(den, 0) <= 0 or num not in avg:
+                return
+            bad = [c for c in (num, den) if c in clamped]
+            derived.append(f"{label} n/a ({' '.join(bad)} clamped)" if bad
+                           else f"{label} {fmt % (avg[num] / avg[den])}")
         derived = []
         if avg.get("TCC_HIT_sum", 0) + avg.get("TCC_MISS_sum", 0) > 0:
             derived.append("L2 hit rate %.3f"
                            % (avg["TCC_HIT_sum"] / (avg["TCC_HIT_sum"] + avg["TCC_MISS_sum"])))
-        if avg.get("SQ_LDS_IDX_ACTIVE", 0) > 0:
-            derived.append("LDS bank-conflict cycles / LDS active cycles %.4f"
-                           % (avg.get("SQ_LDS_BANK_CONFLICT", 0) / avg["SQ_LDS_IDX_ACTIVE"]))
-            derived.append("LDS data-FIFO-full cycles / LDS active cycles %.4f"
-                           % (avg.get("SQ_LDS_DATA_FIFO_FULL", 0) / avg["SQ_LDS_IDX_ACTIVE"]))
-        if avg.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) > 0 and "SQ_VALU_MFMA_COEXEC_CYCLES" in avg:
-            derived.append("VALU co-issued during MFMA-busy cycles %.3f"
-                           % (avg["SQ_VALU_MFMA_COEXEC_CYCLES"] / avg["SQ_VALU_MFMA_BUSY_CYCLES"]))
-        if avg.get("SQ_INSTS_LDS", 0) > 0 and "SQ_WAIT_INST_LDS" in avg:
-            derived.append("wave cycles waiting to issue LDS per LDS instruction %.2f"
-                           % (avg["SQ_WAIT_INST_LDS"] / avg["SQ_INSTS_LDS"]))
+        ratio("LDS bank-conflict cycles / LDS active cycles", "SQ_LDS_BANK_CONFLICT",
+              "SQ_LDS_IDX_ACTIVE", "%.4f")
+        ratio("LDS data-FIFO-full cycles / LDS active cycles", "SQ_LDS_DATA_FIFO_FULL",
+              "SQ_LDS_IDX_ACTIVE", "%.4f")
+        ratio("VALU co-issued during MFMA-busy cycles", "SQ_VALU_MFMA_COEXEC_CYCLES",
+              "SQ_VALU_MFMA_BUSY_CYCLES", "%.3f")
+        ratio("wave cycles waiting to issue LDS per LDS instruction", "SQ_WAIT_INST_LDS",
+              "SQ_INSTS_LDS", "%.2f")
         lines.extend("    " + x for x in derived)
     text = "\n".join(lines) + "\n"
     with open(os.path.join(PROFILES, f"{tag}_{name}.txt"), "w") as f:
         f.write(text)
     return text
+
+
+def _clamped(v: float) -> bool:
+    """A counter value that is a nonzero multiple of 2^24: the counter's limit,
+    not a count (some SQ counters stop there on long kernels)."""
+    return v > 0 and v == int(v) and int(v) % (1 << 24) == 0
 
 
 def summarize_sweep(logs, command: str) -> str:

@@ -35,6 +35,45 @@ __device__ inline __attribute__((always_inline)) void static_for(F&& f) {
   }
 }
 
+// ---- direct global-to-LDS staging (global_load_lds) for the MFMA kernels
+
+// Barrier without the memory fence of __syncthreads: direct-to-LDS loads
+// stay in flight across it (their completion is awaited explicitly before the
+// barrier that publishes them); this wave's LDS reads are complete first.
+__device__ inline void slot_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// One direct global->LDS load: 16 bytes per lane from base + off to LDS byte
+// address lds + 16 * lane (base and lds wave-uniform; lds passed in m0, with
+// the one wait state an LDS DMA needs after m0 is written).  Issued from asm
+// so that the compiler adds no waits of its own for it; every read of the
+// loaded data follows an explicit wait_vm and a barrier.  Nothing else in the
+// kernel keeps a value in m0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved: the asm sets it itself
+__device__ inline void dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+               "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// A wave-uniform pointer moved to scalar registers (for dma16's base where
+// the compiler cannot prove the value uniform).
+template <typename Tp>
+__device__ inline const Tp* uniform_ptr(const Tp* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const Tp*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ inline uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 // Start of shard k of a length-S sequence split n ways: floor(k*S/n).
 __host__ __device__ inline int64_t shard_start(int64_t S, int n, int k) {
   return (int64_t)k * S / n;

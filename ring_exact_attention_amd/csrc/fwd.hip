@@ -170,32 +170,6 @@ __device__ constexpr int kperm(int kb, int m) {
   return C::RPB * (m % C::NBH + C::NBH * (kb % 2)) + m / C::NBH + (16 / C::NBH) * (kb / 2);
 }
 
-// Barrier without the memory fence of __syncthreads: direct-to-LDS loads
-// stay in flight across it (their completion is awaited explicitly before the
-// barrier that publishes them); this wave's LDS reads are complete first.
-__device__ inline void slot_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// One direct global->LDS load: 16 bytes per lane from base + off to LDS byte
-// address lds + 16 * lane (base and lds wave-uniform; lds passed in m0).
-// Issued from asm so that the compiler adds no waits of its own for it; every
-// read of the loaded data follows an explicit wait_vm and a barrier.  Nothing
-// else in the kernel keeps a value in m0.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved: the asm sets it itself
-__device__ inline void dma16(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-__device__ inline uint32_t lds_addr(const char* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)
-template <int N>
-__device__ inline void wait_vm() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
-
 template <int D_>
 __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
   using C = Bf16Fwd<D_>;

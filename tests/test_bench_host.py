@@ -157,3 +157,24 @@ def test_sq_sweep_ratio(tmp_path, profiles):
     rows = [l.split() for l in text.splitlines() if not l.startswith("#")]
     assert [r[0] for r in rows] == ["1024", "2048"]
     assert float(rows[1][-1]) == pytest.approx(4.2 / 2.0 / 2)
+
+
+def test_clamped_counters_give_no_ratio(tmp_path, profiles):
+    # LDS active cycles read 2^29 in every dispatch (the counter's limit on a long
+    # kernel): the ratios over it are withheld; a natural count is kept
+    k = "void bwa::fwd_bf16_kernel<128>(bwa::FwdParams)"
+    rows, cnt = [], []
+    for d in range(3):  # 1 warm-up + 2 timed steps
+        rows.append((d, k, d * 10000, 1000))
+        cnt += [(d, k, "SQ_LDS_IDX_ACTIVE", float(1 << 29)), (d, k, "SQ_LDS_BANK_CONFLICT", 0.0),
+                (d, k, "SQ_LDS_DATA_FIFO_FULL", 5.0), (d, k, "SQ_INSTS_LDS", 1000.0),
+                (d, k, "SQ_WAIT_INST_LDS", 730.0)]
+    _trace(tmp_path / "pmc", rows)
+    _counters(tmp_path / "pmc", cnt)
+    log = _bench_log(tmp_path / "b.log", steps=2, warmup=1)
+    text = bench.summarize_pmc(str(tmp_path / "pmc"), log, "lvx_2k_128k", "lds_counters",
+                               "python3 bench.py")
+    assert "clamped (multiple of 2^24, not a count): SQ_LDS_IDX_ACTIVE" in text
+    assert "LDS bank-conflict cycles / LDS active cycles n/a (SQ_LDS_IDX_ACTIVE clamped)" in text
+    assert "wave cycles waiting to issue LDS per LDS instruction 0.73" in text
+    assert not bench._clamped(123456789.0) and bench._clamped(float(1 << 32))
