@@ -189,6 +189,31 @@ def test_hot_rows_peaked_softmax(bwa, orc):
         check_fwd(o, lse, O, L, "bf16", f"hot rows {mode}")
 
 
+@pytest.mark.parametrize("profile", ["ramp", "jumps"])
+def test_scores_growing_across_tiles(bwa, orc, profile):
+    """Key norms that grow along the sequence (ramp: x1 to x7; jumps: every
+    fifth 64-key tile x6), so that a row's maximum keeps rising from tile to
+    tile: the kernel must move its reference and rescale many times, and
+    between moves accept probabilities far above 1 relative to it."""
+    B, H, SQ, SKV, D = 1, 2, 96, 4096, 128
+    g = torch.Generator().manual_seed(17)
+    q = torch.randn(B, H, SQ, D, generator=g)
+    k = torch.randn(B, H, SKV, D, generator=g)
+    j = torch.arange(SKV, dtype=torch.float32)
+    f = 1 + 6 * j / SKV if profile == "ramp" else torch.where((j // 64) % 5 == 4, 6.0, 1.0)
+    k = k * f[None, None, :, None]
+    v = torch.randn(B, H, SKV, D, generator=g)
+    q, k, v = q.bfloat16(), k.bfloat16(), v.bfloat16()
+    scale = 1 / math.sqrt(D)
+    O, L = orc.attn_fwd(q, k, v, scale)
+    for n in (1, 4):
+        for mode in MODES:
+            log_case(profile=profile, n=n, mode=mode)
+            o, lse = bwa.bwa_ring_fwd(q.cuda(), k.cuda(), v.cuda(), n, "kv", mode, scale=scale)
+            torch.cuda.synchronize()
+            check_fwd(o, lse, O, L, "bf16", f"{profile} n={n} {mode}")
+
+
 def test_deterministic(bwa):
     q, k, v = (x.cuda() for x in gen(1, 4, 512, 4096, 128, torch.bfloat16, seed=5))
     for mode in MODES:
