@@ -126,8 +126,8 @@ __device__ inline void store4<bf16>(bf16* dst, float a, float b, float c, float 
 //
 // 256 query rows per workgroup, 8 waves of 32 rows, 64-key tiles.  A wave's
 // work per tile alternates between an MFMA phase (PV of tile j followed by S
-// of tile j+1) and a VALU phase (mask, max, exp2, row sums and the bf16 P of
-// tile j+1).  Waves 0-3 (group A) and 4-7 (group B) share the four SIMDs one
+// of tile j+1) and a VALU phase (mask, exp2, row sums and the bf16 P of tile
+// j+1; the row maximum only when P grows past the bound below).  Waves 0-3 (group A) and 4-7 (group B) share the four SIMDs one
 // each and run one phase apart: between any two barriers one wave of every
 // SIMD is in its MFMA phase while the other is in its VALU phase, so that
 // the matrix core and the vector ALU can work at the same time.  Barrier intervals
