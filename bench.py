@@ -421,6 +421,49 @@ def summarize_sweep(logs, command: str) -> str:
     return text
 
 
+PHASES = ("valu", "staging", "barrier_open", "mfma", "barrier_close")
+
+
+def summarize_slot_timers(rec, ms_plain: float, ms_timed: float, name: str, mode: str,
+                          command: str) -> str:
+    """Write profiles/slot_timers_<name>.txt from the forward kernel's phase
+    clocks (int64 [workgroups, 2 groups, 6]: five phase sums and the tile
+    count, as bwa_fwd_slot_timers returns them) and the step times of the
+    default and the diagnostic build."""
+    import numpy as np
+    rec = np.asarray(rec, dtype=np.float64)
+    live = rec[(rec[:, 0, 5] > 0) & (rec[:, 1, 5] > 0)]
+    tiles = live[:, 0, 5]
+    lines = [f"# forward kernel phase clocks, workload {name}, mode {mode}: shader-clock cycles "
+             "(s_memtime)",
+             "# per 64-key tile, wave 0 (group A) and wave 4 (group B) of every workgroup, from "
+             "the diagnostic",
+             "# build (libbwa_slot_timers.so, BWA_SLOT_TIMERS=1) of the same kernel source",
+             f"# command: {command}",
+             f"# kernel_hash {kernel_source_hash()}",
+             f"# workgroups with tiles {len(live)} (of {len(rec)} recorded), tiles per workgroup "
+             f"median {np.median(tiles) if len(live) else 0:.0f}",
+             f"# step ms (median): default build {ms_plain:.4f}, diagnostic build {ms_timed:.4f} "
+             f"({(ms_timed / ms_plain - 1) * 100:+.1f}%: the cost of the clock reads)",
+             "# columns: group, phase, cycles per tile: median, 10th and 90th percentile over "
+             "workgroups"]
+    if not len(live):
+        lines.append("no workgroup recorded a tile")
+    for g, gname in ((0, "A"), (1, "B")):
+        per = live[:, g, :5] / live[:, g, 5:6]
+        for i, ph in enumerate(PHASES):
+            x = per[:, i]
+            lines.append(f"{gname} {ph:14s} {np.median(x):8.0f} {np.percentile(x, 10):8.0f} "
+                         f"{np.percentile(x, 90):8.0f}")
+        tot = per.sum(axis=1)
+        lines.append(f"{gname} {'total':14s} {np.median(tot):8.0f} {np.percentile(tot, 10):8.0f} "
+                     f"{np.percentile(tot, 90):8.0f}")
+    text = "\n".join(lines) + "\n"
+    with open(os.path.join(PROFILES, f"slot_timers_{name}.txt"), "w") as f:
+        f.write(text)
+    return text
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -462,6 +505,11 @@ def main():
     ap.add_argument("--summarize-rounds", nargs=2, metavar=("CONTIGUOUS_DIR", "STRIPED_DIR"),
                     help="write profiles/rounds_<workload>.txt from two rocprofv3 kernel traces "
                          "of ROUNDS mode (causal rows in sequence order, then striped) and exit")
+    ap.add_argument("--slot-timers", action="store_true",
+                    help="forward workloads: time the steps with the default library and with "
+                         "its diagnostic build (phase clocks in the forward kernel), then write "
+                         "profiles/slot_timers_<workload>.txt from the clocks of the last step "
+                         "and exit")
     ap.add_argument("--profiled-command", default="python3 bench.py",
                     help="the command line the summarized profiler runs used")
     args = ap.parse_args()
@@ -555,11 +603,38 @@ def main():
         else:
             fwd()
 
+    stream = torch.cuda.current_stream(dev)
+    if args.slot_timers:
+        if recompute or w.dtype != "bf16":
+            print("bench.py: --slot-timers covers the bf16 forward workloads", file=sys.stderr)
+            sys.exit(2)
+
+        def median_ms():
+            for _ in range(args.warmup):
+                step()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+            ev[0].record(stream)
+            for i in range(args.steps):
+                step()
+                ev[i + 1].record(stream)
+            torch.cuda.synchronize()
+            xs = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+            return xs[len(xs) // 2]
+
+        default_lib = _bwa.LIB_PATH
+        ms_plain = median_ms()
+        _bwa.use_library(_bwa.SLOT_TIMERS_LIB_PATH)
+        ms_timed = median_ms()
+        rec = _bwa.fwd_slot_timers()
+        _bwa.use_library(default_lib)
+        command = "python3 bench.py " + " ".join(sys.argv[1:])
+        print(summarize_slot_timers(rec, ms_plain, ms_timed, name, mode, command), flush=True)
+        return
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream(dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
     ev[0].record(stream)

@@ -15,6 +15,9 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libbwa.so")
+# the same library built with the forward kernel's phase clocks (include/bwa_diag.h)
+SLOT_TIMERS_LIB_PATH = os.path.join(_PKG, "libbwa_slot_timers.so")
+SLOT_FIELDS = 6
 
 BWA_OK, BWA_ERR_INVALID_ARG, BWA_ERR_UNSUPPORTED, BWA_ERR_WORKSPACE, BWA_ERR_HIP, \
     BWA_ERR_INTERNAL = range(6)
@@ -33,7 +36,7 @@ EXPORTED = ("bwa_partial_fwd", "bwa_merge", "bwa_merge_partials", "bwa_ring_fwd_
             "bwa_kv_recompute_bwd",
             "bwa_choose_schedule",
             "bwa_status_string",
-            "bwa_last_error", "bwa_version")
+            "bwa_last_error", "bwa_version", "bwa_fwd_slot_timers")
 
 
 class ScheduleModel(ctypes.Structure):
@@ -96,8 +99,33 @@ def lib():
         L.bwa_status_string.restype = ctypes.c_char_p
         L.bwa_last_error.restype = ctypes.c_char_p
         L.bwa_version.restype = ci
+        L.bwa_fwd_slot_timers.argtypes = [vp, i64, ctypes.POINTER(ctypes.c_int64)]
+        L.bwa_fwd_slot_timers.restype = ci
         _lib = L
     return _lib
+
+
+def use_library(path: str):
+    """Load the library from `path` for every later call (for example the
+    diagnostic build at SLOT_TIMERS_LIB_PATH); calls already enqueued are not
+    affected."""
+    global _lib, LIB_PATH
+    LIB_PATH = path
+    _lib = None
+    return lib()
+
+
+def fwd_slot_timers():
+    """Phase clocks of the last bf16 forward launch (diagnostic build only), as
+    an int64 array [records, 2 wave groups, SLOT_FIELDS]; see bwa_fwd_slot_timers."""
+    import numpy as np
+    L = lib()
+    n = ctypes.c_int64(0)
+    probe = (ctypes.c_longlong * (2 * SLOT_FIELDS))()
+    _check(L.bwa_fwd_slot_timers(probe, 0, ctypes.byref(n)))
+    out = np.zeros((n.value, 2, SLOT_FIELDS), dtype=np.int64)
+    _check(L.bwa_fwd_slot_timers(out.ctypes.data, n.value, ctypes.byref(n)))
+    return out
 
 
 def _check(status: int):

@@ -32,6 +32,7 @@
 //
 // fp32 kernel: plain VALU arithmetic (fp32 products and sums), four lanes per
 // query row; used for fp32 inputs where fp32-exact products are required.
+#include "bwa_diag.h"
 #include "common.h"
 
 namespace bwa {
@@ -169,6 +170,86 @@ __device__ constexpr int kperm(int kb, int m) {
   using C = Bf16Fwd<D>;
   return C::RPB * (m % C::NBH + C::NBH * (kb % 2)) + m / C::NBH + (16 / C::NBH) * (kb / 2);
 }
+
+// ---- phase clock of the bf16 kernel's loop.  Compiled in only when the
+// library is built with BWA_SLOT_TIMERS=1 (the diagnostic build); otherwise
+// every member is empty and the kernel is unchanged.  Wave 0 (group A) and
+// wave 4 (group B) sum s_memtime deltas (shader clock cycles) over the tiles
+// they walk: [0] VALU phase (mask, exponentials, row sums, bf16 P), [1] the
+// staging step (wait for the landed tile, issue the next tile's direct
+// loads), [2] the barrier that opens the MFMA slot, [3] the MFMA phase (PV
+// of this tile, S of the next), [4] the barrier that closes it; [5] counts
+// the tiles.  Workgroup w < kSlotRecords writes its two records to
+// fwd_slot_rec[w] at the end (group A then group B); every launch clears the
+// array first.  A stamp is a scalar memory read whose result arrives later,
+// so stamps are only used after the next opening barrier (whose lgkmcnt(0)
+// has waited for them) and a tile's deltas are summed one tile late.  The
+// five stamps per tile still slow the loop down (measured at 2048 x 131072,
+// split mode: one stamp per tile costs nothing, two taken after the barriers
+// about 2%, all five 13-16%), so the phases are those of a slightly slower
+// kernel; the diagnostic summary reports both builds' step times.
+#ifndef BWA_SLOT_TIMERS
+#define BWA_SLOT_TIMERS 0
+#endif
+[[maybe_unused]] constexpr int kSlotRecords = BWA_SLOT_RECORDS;
+[[maybe_unused]] constexpr int kSlotFields = BWA_SLOT_FIELDS;
+#if BWA_SLOT_TIMERS
+__device__ long long fwd_slot_rec[kSlotRecords][2][kSlotFields];
+#endif
+
+struct PhaseClock {
+#if BWA_SLOT_TIMERS
+  // 32-bit stamps and sums (a workgroup's loop lasts far less than 2^32
+  // cycles): fewer scalar registers live across the tile, so that no stamp
+  // has to be moved out of its register (which would wait for it) before the
+  // opening barrier.
+  uint32_t acc[kSlotFields] = {0, 0, 0, 0, 0, 0};
+  // e[i]: stamp after phase i of the current tile (e[4]: of the previous tile
+  // until this tile's closing barrier); e1_prev: e[1] of the previous tile
+  uint32_t e[5] = {0, 0, 0, 0, 0};
+  uint32_t e1_prev = 0;
+  bool open = false;  // e[2..4] hold a tile whose last three deltas are unsummed
+  static __device__ uint32_t now() { return (uint32_t)__builtin_amdgcn_s_memtime(); }
+  __device__ void start() { e[4] = now(); }
+  __device__ void after_valu() { e[0] = now(); }
+  __device__ void after_staging() { e[1] = now(); }
+  // right after the opening barrier: every stamp taken before it has arrived
+  __device__ void after_open() {
+    close_previous();
+    acc[0] += e[0] - e[4];
+    acc[1] += e[1] - e[0];
+    e1_prev = e[1];
+    open = true;
+    e[2] = now();
+  }
+  __device__ void after_mfma() { e[3] = now(); }
+  __device__ void after_close() {
+    e[4] = now();
+    acc[kSlotFields - 1] += 1;
+  }
+  __device__ void close_previous() {
+    if (!open) return;
+    acc[2] += e[2] - e1_prev;
+    acc[3] += e[3] - e[2];
+    acc[4] += e[4] - e[3];
+    open = false;
+  }
+  __device__ void store(int wave, int lane) {
+    close_previous();
+    if (lane != 0 || (wave != 0 && wave != 4) || blockIdx.x >= kSlotRecords) return;
+    long long* rec = fwd_slot_rec[blockIdx.x][wave == 4];
+    for (int i = 0; i < kSlotFields; ++i) rec[i] = acc[i];
+  }
+#else
+  __device__ void start() {}
+  __device__ void after_valu() {}
+  __device__ void after_staging() {}
+  __device__ void after_open() {}
+  __device__ void after_mfma() {}
+  __device__ void after_close() {}
+  __device__ void store(int, int) {}
+#endif
+};
 
 template <int D_>
 __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
@@ -404,6 +485,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
   // visible tiles skips the prologue and the loop altogether (the condition is
   // uniform over the workgroup), so both groups always pass the same barriers.
   TileIter tw = tv;  // latest tile this thread's group has loaded
+  PhaseClock clk;
   if (tv.valid(jb)) {
     dma_tile(tw, 0);
     tw.advance(p, jb, BN);
@@ -436,6 +518,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
       pin(oacc[db][1]);
     }
     int j = 0;
+    clk.start();
     while (tv.valid(jb)) {
       const int cur = j % 3, nxt = (j + 1) % 3;
       phase_softmax(tv);
@@ -446,12 +529,15 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
       }
       pin(lsum[0]);
       pin(lsum[1]);
+      clk.after_valu();
       if (tw.valid(jb)) {  // tile j+1 has landed (published by the barrier below); load tile j+2
         wait_vm<0>();
         tw.advance(p, jb, BN);
         if (tw.valid(jb)) dma_tile(tw, (j + 2) % 3);
       }
+      clk.after_staging();
       slot_barrier();
+      clk.after_open();
       TileIter tn = tv;
       tn.advance(p, jb, BN);
       phase_pv(cur);
@@ -461,12 +547,15 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
         pin(sacc[kb][0]);
         pin(sacc[kb][1]);
       }
+      clk.after_mfma();
       // group A closes this slot; group B's last MFMA slot is the final one
       if (!groupB || tn.valid(jb)) slot_barrier();
+      clk.after_close();
       tv = tn;
       ++j;
     }
   }  // tv.valid(jb)
+  clk.store(wave, lane);
 
   // ---- epilogue: a row's sum is spread over the four lanes of its column
 #pragma unroll
@@ -626,6 +715,14 @@ int fwd_tile_rows(int dtype_bf16, int D) {
 hipError_t fwd_launch(FwdParams p, int dtype_bf16, hipStream_t st) {
   const int blocks = xcd_grid_size(p.tiles, p.groups);
   if (blocks == 0) return hipSuccess;
+#if BWA_SLOT_TIMERS
+  if (dtype_bf16) {
+    void* rec = nullptr;
+    hipError_t e = hipGetSymbolAddress(&rec, HIP_SYMBOL(fwd_slot_rec));
+    if (e == hipSuccess) e = hipMemsetAsync(rec, 0, sizeof(fwd_slot_rec), st);
+    if (e != hipSuccess) return e;
+  }
+#endif
   if (dtype_bf16) {
     if (p.D == 128)
       hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3(blocks), dim3(Bf16Fwd<128>::NT), 0, st, p);
@@ -641,3 +738,20 @@ hipError_t fwd_launch(FwdParams p, int dtype_bf16, hipStream_t st) {
 }
 
 }  // namespace bwa
+
+extern "C" int bwa_fwd_slot_timers(long long* out, int64_t max_records, int64_t* n_records) {
+  if (!out || !n_records || max_records < 0) return BWA_ERR_INVALID_ARG;
+#if BWA_SLOT_TIMERS
+  const int64_t n = max_records < bwa::kSlotRecords ? max_records : bwa::kSlotRecords;
+  *n_records = bwa::kSlotRecords;
+  if (hipDeviceSynchronize() != hipSuccess) return BWA_ERR_HIP;
+  if (n > 0 && hipMemcpyFromSymbol(out, HIP_SYMBOL(bwa::fwd_slot_rec),
+                                   n * 2 * bwa::kSlotFields * sizeof(long long), 0,
+                                   hipMemcpyDeviceToHost) != hipSuccess)
+    return BWA_ERR_HIP;
+  return BWA_OK;
+#else
+  *n_records = 0;
+  return BWA_ERR_UNSUPPORTED;
+#endif
+}

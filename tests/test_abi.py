@@ -4,6 +4,7 @@ No compute call is made here (there is no GPU in this suite): every call
 below fails validation on the host, before anything could be enqueued.
 """
 import ctypes
+import glob
 import os
 import re
 
@@ -12,15 +13,17 @@ import pytest
 from ring_exact_attention_amd import _bwa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "bwa.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 FAKE = 0x7F0000000000  # an aligned address that is never dereferenced
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(bwa_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(bwa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -39,9 +42,19 @@ def T(B=1, H=2, S=64, D=128, dtype=_bwa.BWA_BF16, ptr=FAKE, strides=None):
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert set(_bwa.EXPORTED) <= set(names)
+    assert "bwa_fwd_slot_timers" in names  # the diagnostic header is scanned too
     for name in names:
         assert hasattr(L, name), name
     assert L.bwa_version() == 1
+
+
+def test_slot_timers_unsupported_in_default_build(L):
+    out = (ctypes.c_longlong * 12)()
+    n = ctypes.c_int64(-1)
+    assert L.bwa_fwd_slot_timers(out, 1, ctypes.byref(n)) == _bwa.BWA_ERR_UNSUPPORTED
+    assert n.value == 0
+    assert L.bwa_fwd_slot_timers(None, 1, ctypes.byref(n)) == _bwa.BWA_ERR_INVALID_ARG
+    assert L.bwa_fwd_slot_timers(out, -1, ctypes.byref(n)) == _bwa.BWA_ERR_INVALID_ARG
 
 
 def test_status_strings(L):

@@ -178,3 +178,24 @@ def test_clamped_counters_give_no_ratio(tmp_path, profiles):
     assert "LDS bank-conflict cycles / LDS active cycles n/a (SQ_LDS_IDX_ACTIVE clamped)" in text
     assert "wave cycles waiting to issue LDS per LDS instruction 0.73" in text
     assert not bench._clamped(123456789.0) and bench._clamped(float(1 << 32))
+
+
+def test_slot_timer_summary(tmp_path, profiles, monkeypatch):
+    import numpy as np
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "h0")
+    # 4 workgroups of 256 tiles and one without tiles; group A spends 1000 cycles
+    # per tile in its VALU phase and 2000 in its MFMA phase, group B twice that
+    rec = np.zeros((5, 2, 6), dtype=np.int64)
+    for w in range(4):
+        rec[w, 0] = [1000 * 256, 100 * 256, 50 * 256, 2000 * 256, 10 * 256, 256]
+        rec[w, 1] = [2000 * 256, 200 * 256, 100 * 256, 4000 * 256, 20 * 256, 256]
+    text = bench.summarize_slot_timers(rec, 4.0, 4.2, "lvx_2k_128k", "split",
+                                       "python3 bench.py --slot-timers")
+    rows = {tuple(l.split()[:2]): [float(x) for x in l.split()[2:]]
+            for l in text.splitlines() if not l.startswith("#")}
+    assert rows[("A", "valu")] == [1000.0, 1000.0, 1000.0]
+    assert rows[("B", "mfma")][0] == 4000.0
+    assert rows[("A", "total")][0] == 3160.0 and rows[("B", "total")][0] == 6320.0
+    assert "workgroups with tiles 4 (of 5 recorded)" in text
+    assert "+5.0%" in text
+    assert (profiles / "slot_timers_lvx_2k_128k.txt").read_text() == text

@@ -223,6 +223,38 @@ def test_deterministic(bwa):
         assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), mode
 
 
+def test_slot_timer_build_is_bitwise_default(bwa):
+    """The diagnostic build (phase clocks in the forward kernel) computes what
+    the default build computes, bit for bit, and records every workgroup's
+    tiles: in split mode at n = 4 over 512 rows x 4096 keys a workgroup takes
+    256 query rows against one KV shard, so 2 heads x 4 shards x 2 row tiles
+    = 16 workgroups, each walking 1024 / 64 = 16 key tiles."""
+    from ring_exact_attention_amd import _bwa
+    q, k, v = (x.cuda() for x in gen(1, 2, 512, 4096, 128, torch.bfloat16, seed=41))
+    qc, kc, vc = (x.cuda() for x in gen(1, 2, 1024, 1024, 128, torch.bfloat16, seed=42))
+    default = _bwa.LIB_PATH
+    ref = [bwa.bwa_ring_fwd(q, k, v, 4, "kv", "split"),
+           bwa.bwa_ring_fwd(qc, kc, vc, 4, "q", "fused", causal=True)]
+    torch.cuda.synchronize()
+    try:
+        _bwa.use_library(_bwa.SLOT_TIMERS_LIB_PATH)
+        log_case(test="slot_timers", mode="split")
+        o, lse = bwa.bwa_ring_fwd(q, k, v, 4, "kv", "split")
+        rec = _bwa.fwd_slot_timers()
+        assert torch.equal(o, ref[0][0]) and torch.equal(lse, ref[0][1])
+        live = rec[rec[:, 0, 5] > 0]
+        assert len(live) == 16
+        assert (live[:, :, 5] == 16).all()
+        assert (live[:, :, :5] >= 0).all() and (live[:, :, 3] > 0).all()
+        log_case(test="slot_timers", mode="fused", causal=True)
+        o, lse = bwa.bwa_ring_fwd(qc, kc, vc, 4, "q", "fused", causal=True)
+        rec = _bwa.fwd_slot_timers()
+        assert torch.equal(o, ref[1][0]) and torch.equal(lse, ref[1][1])
+        assert rec[:, :, 5].sum() > 0
+    finally:
+        _bwa.use_library(default)
+
+
 def test_schedules_agree_closely(bwa, orc):
     """Both schedules and all modes compute the same pairs.  They differ in
     fp32 merge order and, more, in the reference maximum each probability is
