@@ -79,6 +79,43 @@ def test_bwd_small(bwa, orc, shape):
             check_grad(dv.reshape(B * H, SKV, D), ref["dv"], f"dv {shape} {mode}/{sched}")
 
 
+@pytest.mark.parametrize("shape", [(2, 3, 130, 700, 4, False, 128), (1, 2, 300, 300, 3, True, 128),
+                                   (2, 2, 200, 450, 3, False, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_bwd_strided_layouts_and_guard_bands(bwa, orc, shape):
+    """Every input and gradient in [B, S, H, D] storage viewed as [B, H, S, D];
+    each gradient written into the middle of a NaN-filled buffer, whose rest
+    must stay untouched."""
+    B, H, SQ, SKV, n, causal, D = shape
+    scale = 1 / math.sqrt(D)
+    q, k, v, do = gen(B, H, SQ, SKV, D, seed=SQ * 7 + SKV + D)
+    ref = orc.attn_bwd(q, k, v, do, scale, causal)
+    extra = dq_row_allowance(orc, q, k, v, do, scale, causal)
+    bshd = lambda t: t.transpose(1, 2).contiguous().cuda().transpose(1, 2)
+    qs, ks, vs, dos = bshd(q), bshd(k), bshd(v), bshd(do)
+    o, lse = bwa.bwa_ring_fwd(q.cuda(), k.cuda(), v.cuda(), n, "kv", "fused", causal=causal,
+                              scale=scale)
+    os_ = bshd(o.cpu())
+
+    def guarded(S):
+        big = torch.full((B, S + 8, H, D + 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+        return big, big[:, 4:4 + S, :, 32:32 + D].transpose(1, 2)
+
+    for mode in ("fused", "rounds"):
+        for sched in ("kv", "q"):
+            log_case(strided=shape, mode=mode, sched=sched)
+            (bq, gq), (bk, gk), (bv, gv) = guarded(SQ), guarded(SKV), guarded(SKV)
+            bwa.bwa_ring_bwd(qs, ks, vs, os_, lse, dos, n, sched, mode, causal=causal, scale=scale,
+                             dq=gq, dk=gk, dv=gv)
+            torch.cuda.synchronize()
+            for big, g, name, S in ((bq, gq, "dq", SQ), (bk, gk, "dk", SKV), (bv, gv, "dv", SKV)):
+                check_grad(g.reshape(B * H, S, D), ref[name], f"{name} strided {shape} {mode}/{sched}",
+                           row_extra=extra if name == "dq" else None)
+                mask = torch.ones_like(big, dtype=torch.bool)
+                mask[:, 4:4 + S, :, 32:32 + D] = False
+                assert torch.isnan(big[mask].float()).all(), f"{name}: write outside the view"
+
+
 def test_bwd_deterministic(bwa):
     q, k, v, do = (x.cuda() for x in gen(1, 2, 512, 4096, 128, seed=1))
     o, lse = bwa.bwa_ring_fwd(q, k, v, 8)
