@@ -54,6 +54,12 @@ bwa_status hip_fail(hipError_t e, const char* what) {
 size_t elem_size(int32_t dt) { return dt == BWA_BF16 ? 2 : 4; }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
+// Rows over all (batch, head) pairs of one tensor: row-parallel kernels launch
+// one thread per 4 to 16 elements of a row, and their grids stay below 2^31.
+constexpr int64_t kMaxRows = (int64_t)1 << 33;
+// Workgroups of any one launch (gridDim.x must stay below 2^31; the XCD-aware
+// mapping rounds the group count up to a multiple of 8).
+constexpr int64_t kMaxGrid = (int64_t)1 << 30;
 
 // Structural checks shared by every tensor argument.
 bwa_status check_tensor(const bwa_tensor* t, const char* name, bool allow_empty_seq) {
@@ -69,6 +75,8 @@ bwa_status check_tensor(const bwa_tensor* t, const char* name, bool allow_empty_
                 (long long)t->D);
   if (t->B * t->H >= kMaxDim || t->S >= kMaxDim)
     return fail(BWA_ERR_UNSUPPORTED, "%s: sizes beyond 2^31 rows", name);
+  if (t->B * t->H * t->S > kMaxRows)
+    return fail(BWA_ERR_UNSUPPORTED, "%s: more than 2^33 rows over all heads", name);
   if (t->sB < 0 || t->sH < 0 || t->sS < 0)
     return fail(BWA_ERR_INVALID_ARG, "%s: negative stride", name);
   if (t->S == 0) return BWA_OK;
@@ -166,10 +174,16 @@ bwa_status check_ring(const bwa_tensor* q, const bwa_tensor* k, int n, int mode)
     return fail(BWA_ERR_INVALID_ARG, "n = %d shards must be in [1, S_KV = %lld]", n,
                 (long long)k->S);
   if (n > 4096) return fail(BWA_ERR_UNSUPPORTED, "n = %d above 4096", n);
+  // Largest grid of any ring launch: at most (B*H + 7) * n groups of at most
+  // ceil(ceil(S / n) / 64) tiles (64 rows is the smallest tile of any kernel).
+  const int64_t S = q->S > k->S ? q->S : k->S;
+  const int64_t tiles = ((S + n - 1) / n + 63) / 64;
+  if ((q->B * q->H + 7) * n * tiles > kMaxGrid)
+    return fail(BWA_ERR_UNSUPPORTED, "B*H*n = %lld pairs of shards need a grid above 2^30",
+                (long long)(q->B * q->H * n));
   if (mode != BWA_MODE_ROUNDS && mode != BWA_MODE_FUSED && mode != BWA_MODE_SPLIT &&
       mode != BWA_MODE_ROUNDS_TRANSFER)
     return fail(BWA_ERR_INVALID_ARG, "unknown mode %d", mode);
-  (void)q;
   return BWA_OK;
 }
 
@@ -239,6 +253,8 @@ bwa_status bwa_partial_fwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_t
     return fail(BWA_ERR_INVALID_ARG, "key range [%lld, %lld) outside [0, %lld)", (long long)k0,
                 (long long)(k0 + nk), (long long)k->S);
   if (nq == 0) return BWA_OK;
+  if ((q->B * q->H + 7) * ((nq + 63) / 64) > kMaxGrid)
+    return fail(BWA_ERR_UNSUPPORTED, "B*H*nq needs a grid above 2^30");
   if (!o_acc || !lse_acc) return fail(BWA_ERR_INVALID_ARG, "o_acc / lse_acc is NULL");
   if ((uintptr_t)o_acc % 16 != 0) return fail(BWA_ERR_UNSUPPORTED, "o_acc must be 16-byte aligned");
   bwa::FwdParams p = base_params(q, k, v, scale, causal);
@@ -261,6 +277,7 @@ bwa_status bwa_merge(int64_t rows, int64_t D, const float* o_a, const float* lse
                      const float* o_b, const float* lse_b, float* o_out, float* lse_out,
                      void* stream) {
   if (rows < 0) return fail(BWA_ERR_INVALID_ARG, "rows < 0");
+  if (rows > kMaxRows) return fail(BWA_ERR_UNSUPPORTED, "more than 2^33 rows");
   if (D != 64 && D != 128) return fail(BWA_ERR_UNSUPPORTED, "D must be 64 or 128");
   if (rows == 0) return BWA_OK;
   if (!o_a || !lse_a || !o_b || !lse_b || !o_out || !lse_out)

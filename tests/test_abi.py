@@ -101,6 +101,13 @@ def test_ring_fwd_validation(L):
     expect(L, ring_fwd(L, q, T(H=3, S=256), T(H=3, S=256), o), E.BWA_ERR_INVALID_ARG, "head")
     big = T(S=256, strides=(2 * (1 << 23), 1 << 23, 1 << 23))  # 16 MiB rows (bf16)
     expect(L, ring_fwd(L, q, big, k, o), E.BWA_ERR_UNSUPPORTED, "row stride")
+    # heads broadcast through zero strides: sizes whose grids would overflow are refused
+    z = (0, 0, 0)
+    expect(L, ring_fwd(L, T(H=1 << 28, S=64, strides=z), T(H=1 << 28, S=256, strides=z),
+                       T(H=1 << 28, S=256, strides=z), T(H=1 << 28, S=64, strides=z)),
+           E.BWA_ERR_UNSUPPORTED, "2^33 rows")
+    hq, hk = T(H=1 << 21, S=1, strides=z), T(H=1 << 21, S=4096, strides=z)
+    expect(L, ring_fwd(L, hq, hk, hk, hq, n=4096), E.BWA_ERR_UNSUPPORTED, "grid above 2^30")
 
 
 def test_transfer_workspace_covers_both_schedules(L):
@@ -148,6 +155,11 @@ def test_partial_fwd_validation(L):
                 FAKE + 4, FAKE, 0, None), E.BWA_ERR_UNSUPPORTED, "aligned")
     assert f(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), 5, 0, 0, 16, 0.1, 0, None, None,
              0, None) == E.BWA_OK
+    # 2^30 heads broadcast through zero strides: the grid would pass 2^30 workgroups
+    z = (0, 0, 0)
+    hq, hk = T(H=1 << 30, S=1, strides=z), T(H=1 << 30, S=2, strides=z)
+    expect(L, f(ctypes.byref(hq), ctypes.byref(hk), ctypes.byref(hk), 0, 1, 0, 2, 0.1, 0, FAKE,
+                FAKE, 0, None), E.BWA_ERR_UNSUPPORTED, "grid above 2^30")
 
 
 def test_merge_validation(L):
@@ -161,6 +173,8 @@ def test_merge_validation(L):
            "D must")
     expect(L, L.bwa_merge(-1, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None),
            E.BWA_ERR_INVALID_ARG, "rows")
+    expect(L, L.bwa_merge((1 << 33) + 1, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None),
+           E.BWA_ERR_UNSUPPORTED, "2^33 rows")
     expect(L, L.bwa_merge(4, 64, None, FAKE, FAKE, FAKE, FAKE, FAKE, None), E.BWA_ERR_INVALID_ARG,
            "NULL")
     assert L.bwa_merge(0, 64, None, None, None, None, None, None, None) == E.BWA_OK
