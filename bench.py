@@ -97,6 +97,19 @@ def cpu_baseline(q, k, v, w, rows_per_head: int):
     import numpy as np
 
     import oracle
+    if w.dtype != "bf16":
+        # latency-bound fp32 workload: the whole problem, as time per call
+        qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+        oracle.attn_fwd(qc, kc, vc, w.scale, causal=w.causal)
+        reps = 20
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.attn_fwd(qc, kc, vc, w.scale, causal=w.causal)
+        dt = (time.perf_counter() - t0) / reps
+        return {"value": round(dt * 1e6, 1), "unit": "us", "cores": oracle.num_threads(),
+                "kind": "oracle",
+                "sample": f"the whole problem ({w.B * w.H * w.SQ} rows x {w.SKV} keys), fp64, "
+                          f"mean of {reps} calls"}
     g = np.random.default_rng(w.seed)
     rows = []
     for bh in range(w.B * w.H):
@@ -484,6 +497,9 @@ def main():
     ap.add_argument("--weight-grads", action="store_true",
                     help="recompute workload: also run the gradients through the projection "
                          "(dW_k, dW_v, dy) in every step")
+    ap.add_argument("--graph", action="store_true",
+                    help="record one step into a HIP graph (torch.cuda.CUDAGraph over the "
+                         "library's stream) and time its replays instead of eager calls")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy one 1 GiB buffer (a plain copy kernel of "
                          "known size, to calibrate HBM byte counters taken under a profiler)")
@@ -634,6 +650,25 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.graph:
+        # every buffer of a step is allocated above, so a step records as kernels
+        # (and, in the transfer mode, device copies) only
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        eager_step = step
+        step = graph.replay  # noqa: F811  (the timed loop below replays the graph)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        del eager_step
 
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
@@ -668,7 +703,14 @@ def main():
     # in split mode one launch plus the merge.  Per-launch work is the step's
     # work divided by the launches of that kernel.
     launches = w.n if mode in ("rounds", "rounds_transfer") else 1
-    if recompute:
+    if w.dtype != "bf16":
+        # fp32 tiny workload: launch- and latency-bound (a few microseconds of work),
+        # reported as time per call; no roofline claim
+        roofline = {"bound": "latency", "achieved": None, "peak": None, "unit": "us",
+                    "frac": None, "traffic": None, "kernel": f"fwd_f32_kernel<{w.D}>",
+                    "launches_per_step": w.n if mode in ("rounds", "rounds_transfer") else 1,
+                    "us_per_step": round(ms * 1e3, 2)}
+    elif recompute:
         # several kernels per step (GEMM, forward, backward); report the step as a whole
         roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
@@ -714,18 +756,20 @@ def main():
             roofline = {"bound": "mfma", "achieved": round(achieved, 2),
                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
-        roofline.update({"kernel": "fwd_bf16_kernel<128>", "launches_per_step": launches,
+        roofline.update({"kernel": f"fwd_bf16_kernel<{w.D}>", "launches_per_step": launches,
                          "kernel_ms_per_launch": round(kernel_ms, 4),
                          "other_ms_per_step": round(ms - fwd_ms, 4),
                          "mfma_busy_profiled": busy, "clock_ghz_profiled": clock})
 
+    latency = w.dtype != "bf16"
     out = {
         "metric": METRIC if (args.workload == "lvx_2k_128k" and not args.sq) else
-        f"{'training-step' if recompute else 'attention'} TFLOP/s, {w.name}"
-        f"{' with weight gradients' if args.weight_grads else ''}"
-        f"{f' at S_Q={w.SQ}' if args.sq else ''}, 1 GPU",
-        "value": round(tflops, 2),
-        "unit": "TFLOP/s",
+        (f"attention time per call (us), {w.name}, 1 GPU" if latency else
+         f"{'training-step' if recompute else 'attention'} TFLOP/s, {w.name}"
+         f"{' with weight gradients' if args.weight_grads else ''}"
+         f"{f' at S_Q={w.SQ}' if args.sq else ''}, 1 GPU"),
+        "value": round(ms * 1e3, 2) if latency else round(tflops, 2),
+        "unit": "us" if latency else "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -734,7 +778,7 @@ def main():
         "ms_per_step_max": round(per_step_ms[-1], 4),
         "ms_per_step_mean": round(ms_mean, 4),
         "wall_s_timed": round(wall, 4),
-        "higher_is_better": True,
+        "higher_is_better": not latency,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
@@ -742,7 +786,7 @@ def main():
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "S_Q": w.SQ, "S_KV": w.SKV, "D": w.D,
                    "n_shards": w.n, "schedule": args.sched, "mode": mode, "causal": causal,
-                   "seed": w.seed},
+                   "seed": w.seed, "graph": args.graph},
         "roofline": roofline,
     }
     if not recompute:

@@ -643,30 +643,49 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
   it.seek(p, jb, 0, BN);
   if (!it.valid(jb) && jb.epi == EPI_ACC && jb.acc_in) return;
   const float c2 = p.scale_log2;
-  for (; it.valid(jb); it.advance(p, jb, BN)) {
+  // Staging: thread tid moves 16-byte chunks tid + i NT (i < NCH) of a tile's
+  // K and V (row c / (D/4), column chunk c % (D/4)); keys at or past the
+  // segment end are zero.  The next tile's chunks are loaded into registers
+  // while the current tile is computed.
+  constexpr int NCH = BN * D / 4 / C::NT;
+  static_assert(NCH * C::NT == BN * D / 4, "staging split");
+  f32x4 kx[NCH], vx[NCH];
+  auto load = [&](const TileIter& t) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + i * C::NT, row = c / (D / 4), col4 = c % (D / 4);
+      const int64_t key = t.kt + row;
+      kx[i] = key < t.ke ? *(const f32x4*)(kg + key * p.skS + col4 * 4) : f32x4{};
+      vx[i] = key < t.ke ? *(const f32x4*)(vg + key * p.svS + col4 * 4) : f32x4{};
+    }
+  };
+  // sum over the four lanes of a row (lanes 4r .. 4r+3): quad permutations
+  auto quad_sum = [](float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+  };
+  if (it.valid(jb)) load(it);
+  while (it.valid(jb)) {
     // keys it.kt + j, j < lim, are visible to this row
     const int lim = visible_prefix(it.kt, it.ke, p.causal, myrow, BN, p.blk, row_w, row_c);
-    __syncthreads();
-    for (int c = tid; c < BN * D / 4; c += C::NT) {
-      int row = c / (D / 4), col4 = c % (D / 4);
-      int64_t key = it.kt + row;
-      f32x4 kx = f32x4{}, vx = f32x4{};
-      if (key < it.ke) {
-        kx = *(const f32x4*)(kg + key * p.skS + col4 * 4);
-        vx = *(const f32x4*)(vg + key * p.svS + col4 * 4);
-      }
-      *(f32x4*)(Ks + row * KS + col4 * 4) = kx;
-      *(f32x4*)(Vs + row * KS + col4 * 4) = vx;
+    __syncthreads();  // every read of the previous tile is done
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + i * C::NT, row = c / (D / 4), col4 = c % (D / 4);
+      *(f32x4*)(Ks + row * KS + col4 * 4) = kx[i];
+      *(f32x4*)(Vs + row * KS + col4 * 4) = vx[i];
     }
     __syncthreads();
+    TileIter nx = it;
+    nx.advance(p, jb, BN);
+    if (nx.valid(jb)) load(nx);
     // one key at a time: score, then the online-softmax update of (m, l, acc)
-#pragma unroll 2
+#pragma unroll 8
     for (int j = 0; j < BN; ++j) {
       float dot = 0.f;
 #pragma unroll
       for (int e = 0; e < DL; ++e) dot = __builtin_fmaf(qv[e], Ks[j * KS + sub * DL + e], dot);
-      dot += __shfl_xor(dot, 1);
-      dot += __shfl_xor(dot, 2);
+      dot = quad_sum(dot);
       if (j >= lim) continue;  // uniform across the four lanes of a row
       const float t = dot * c2;
       const float m_new = fmaxf(m2, t);
@@ -678,6 +697,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
       for (int e = 0; e < DL; ++e)
         acc[e] = __builtin_fmaf(pj, Vs[j * KS + sub * DL + e], acc[e] * alpha);
     }
+    it = nx;
   }
 
   const bool empty = (m2 == -INFINITY) || !(l > 0.f);
