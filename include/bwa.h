@@ -33,7 +33,7 @@
  *     The base pointer must be 16-byte aligned and sB, sH, sS multiples of
  *     16 bytes; a row (sS) spans less than 16 MiB.  D must be 64 or 128.
  *   - Sizes: B*H and S below 2^31, B*H*S at most 2^33 rows per tensor, and
- *     B*H*n times the 64-row tiles of a shard at most 2^30 (the largest
+ *     B*H*n times the 16-row tiles of a shard at most 2^30 (the largest
  *     launch grid); larger calls (reachable only with broadcast zero
  *     strides) return BWA_ERR_UNSUPPORTED.
  *   - scale is the softmax scale (callers pass 1/sqrt(D)); it must be finite

@@ -175,9 +175,9 @@ bwa_status check_ring(const bwa_tensor* q, const bwa_tensor* k, int n, int mode)
                 (long long)k->S);
   if (n > 4096) return fail(BWA_ERR_UNSUPPORTED, "n = %d above 4096", n);
   // Largest grid of any ring launch: at most (B*H + 7) * n groups of at most
-  // ceil(ceil(S / n) / 64) tiles (64 rows is the smallest tile of any kernel).
+  // ceil(ceil(S / n) / 16) tiles (16 rows is the smallest tile of any kernel).
   const int64_t S = q->S > k->S ? q->S : k->S;
-  const int64_t tiles = ((S + n - 1) / n + 63) / 64;
+  const int64_t tiles = ((S + n - 1) / n + 15) / 16;
   if ((q->B * q->H + 7) * n * tiles > kMaxGrid)
     return fail(BWA_ERR_UNSUPPORTED, "B*H*n = %lld pairs of shards need a grid above 2^30",
                 (long long)(q->B * q->H * n));
@@ -253,7 +253,7 @@ bwa_status bwa_partial_fwd(const bwa_tensor* q, const bwa_tensor* k, const bwa_t
     return fail(BWA_ERR_INVALID_ARG, "key range [%lld, %lld) outside [0, %lld)", (long long)k0,
                 (long long)(k0 + nk), (long long)k->S);
   if (nq == 0) return BWA_OK;
-  if ((q->B * q->H + 7) * ((nq + 63) / 64) > kMaxGrid)
+  if ((q->B * q->H + 7) * ((nq + 15) / 16) > kMaxGrid)
     return fail(BWA_ERR_UNSUPPORTED, "B*H*nq needs a grid above 2^30");
   if (!o_acc || !lse_acc) return fail(BWA_ERR_INVALID_ARG, "o_acc / lse_acc is NULL");
   if ((uintptr_t)o_acc % 16 != 0) return fail(BWA_ERR_UNSUPPORTED, "o_acc must be 16-byte aligned");

@@ -591,13 +591,20 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
 
 // ------------------------------------------------------------------ fp32 VALU kernel
 
+// x of the lane that DPP control CTRL selects (every lane active)
+template <int CTRL>
+__device__ inline float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
 template <int D>
 struct F32Fwd {
-  static constexpr int BN = 32;   // keys per tile
-  static constexpr int BM = 64;   // query rows per workgroup (4 lanes per row)
-  static constexpr int NT = 256;
-  static constexpr int DL = D / 4;  // dims per lane
-  static constexpr int KS = D + 4;  // LDS row stride (floats)
+  static constexpr int BN = 32;    // keys per tile
+  static constexpr int LPR = 16;   // lanes per query row (one DPP row)
+  static constexpr int BM = 16;    // query rows per workgroup
+  static constexpr int NT = BM * LPR;
+  static constexpr int DL = D / LPR;  // dims per lane
+  static constexpr int KS = D + 4;    // LDS row stride (floats)
 };
 
 template <int D>
@@ -610,8 +617,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
   Job jb;
   if (!make_job(p, C::BM, &jb)) return;
   const int tid = threadIdx.x;
-  const int sub = tid & 3;  // which quarter of D this lane owns
-  const int64_t myrow = jb.r0 + (tid >> 2);
+  const int sub = tid % C::LPR;  // which DL dims of the row this lane owns
+  const int64_t myrow = jb.r0 + tid / C::LPR;
   const bool row_ok = myrow < jb.r1;
   const int64_t row_w = p.causal == 2 ? myrow / p.blk : 0;  // striped: shard, index
   const int64_t row_c = p.causal == 2 ? myrow - row_w * p.blk : 0;
@@ -659,10 +666,15 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
       vx[i] = key < t.ke ? *(const f32x4*)(vg + key * p.svS + col4 * 4) : f32x4{};
     }
   };
-  // sum over the four lanes of a row (lanes 4r .. 4r+3): quad permutations
-  auto quad_sum = [](float x) {
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
-    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+  // sum over the 16 lanes of a row (one DPP row): lane pairs l^1 and l^2
+  // (quad permutations), then l <-> 7-l within each half row and l <-> 15-l;
+  // each step adds two equal-by-construction partial sums, so every lane of
+  // the row ends with the same bits
+  auto row_sum = [](float x) {
+    x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_f32<0x141>(x);  // row_half_mirror
+    return x + dpp_f32<0x140>(x);  // row_mirror
   };
   if (it.valid(jb)) load(it);
   while (it.valid(jb)) {
@@ -679,18 +691,20 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
     TileIter nx = it;
     nx.advance(p, jb, BN);
     if (nx.valid(jb)) load(nx);
-    // one key at a time: score, then the online-softmax update of (m, l, acc)
+    // one key at a time: score, then the online-softmax update of (m, l,
+    // acc).  A key at or past lim leaves them exactly as they are (alpha = 1,
+    // p = 0); selects rather than a branch let the unrolled keys overlap.
 #pragma unroll 8
     for (int j = 0; j < BN; ++j) {
       float dot = 0.f;
 #pragma unroll
       for (int e = 0; e < DL; ++e) dot = __builtin_fmaf(qv[e], Ks[j * KS + sub * DL + e], dot);
-      dot = quad_sum(dot);
-      if (j >= lim) continue;  // uniform across the four lanes of a row
-      const float t = dot * c2;
+      dot = row_sum(dot);
+      const bool vis = j < lim;
+      const float t = vis ? dot * c2 : -INFINITY;
       const float m_new = fmaxf(m2, t);
-      const float alpha = fast_exp2(m2 - m_new);
-      const float pj = fast_exp2(t - m_new);
+      const float alpha = vis ? fast_exp2(m2 - m_new) : 1.f;
+      const float pj = vis ? fast_exp2(t - m_new) : 0.f;
       m2 = m_new;
       l = l * alpha + pj;
 #pragma unroll
