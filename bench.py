@@ -663,12 +663,10 @@ def main():
         with torch.cuda.graph(graph):
             step()
         torch.cuda.synchronize()
-        eager_step = step
         step = graph.replay  # noqa: F811  (the timed loop below replays the graph)
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
-        del eager_step
 
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
