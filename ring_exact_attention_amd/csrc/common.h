@@ -195,6 +195,9 @@ __device__ inline bool make_job(const FwdParams& p, int BM, Job* jb) {
     jb->nseg = p.n;
     jb->epi = EPI_FINAL;
     jb->acc_in = false;
+    // and within a block later rows see more keys (in either causal order):
+    // its row tiles go last to first
+    if (p.causal) t = p.tiles - 1 - t;
   }
   jb->block = j;
   int64_t qs = shard_start(p.SQ, p.n, j), qe = shard_start(p.SQ, p.n, j + 1);
@@ -232,14 +235,23 @@ __device__ inline void job_segment(const FwdParams& p, const Job& jb, int r, int
 struct TileIter {
   int r;           // segment step
   int64_t kt, ke;  // current tile start, end of current segment
+  // start of the current segment and, in the striped order, the shard it
+  // starts (every segment there begins at a shard start)
+  int64_t s0, sk;
   __device__ inline void seek(const FwdParams& p, const Job& jb, int from, int BN) {
     (void)BN;
     for (r = from; r < jb.nseg; ++r) {
       int64_t a, b;
       job_segment(p, jb, r, &a, &b);
-      if (b > a) { kt = a; ke = b; return; }
+      if (b > a) {
+        kt = a;
+        ke = b;
+        s0 = a;
+        sk = p.causal == 2 ? a / p.blk : 0;
+        return;
+      }
     }
-    kt = ke = 0;
+    kt = ke = s0 = sk = 0;
   }
   __device__ inline bool valid(const Job& jb) const { return r < jb.nseg; }
   __device__ inline void advance(const FwdParams& p, const Job& jb, int BN) {

@@ -68,22 +68,22 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// Number of leading keys of a tile starting at key kt that a query row may see:
-// keys kt .. kt+lim-1 are visible (segment end ke; under causal masking only
-// keys at or before the row's position).  Clamped to [0, bn].
+// Number of leading keys of tile t that a query row may see: keys t.kt ..
+// t.kt+lim-1 are visible (segment end t.ke; under causal masking only keys at
+// or before the row's position).  Clamped to [0, bn].
 //   causal == 1: rows and keys in sequence order, key j visible iff j <= row.
 //   causal == 2: striped order over shards of blk rows (shard w holds
 //     positions w, w+n, ...): the row at (shard w, index c) sees the first
 //     c + 1 keys of shards <= w and the first c keys of later shards; a tile
-//     lies inside one shard (ks, starting at index c0).  (row_w, row_c) is the
-//     row's (shard, index).
-__device__ inline int visible_prefix(int64_t kt, int64_t ke, int causal, int64_t row, int bn,
-                                     int64_t blk, int64_t row_w, int64_t row_c) {
-  int64_t lim = ke - kt;
-  if (causal == 1 && row + 1 - kt < lim) lim = row + 1 - kt;
+//     lies inside one segment, which starts at the start t.s0 of shard t.sk,
+//     so the tile's first key has index t.kt - t.s0 in that shard.
+//     (row_w, row_c) is the row's (shard, index).
+__device__ inline int visible_prefix(const TileIter& t, int causal, int64_t row, int bn,
+                                     int64_t row_w, int64_t row_c) {
+  int64_t lim = t.ke - t.kt;
+  if (causal == 1 && row + 1 - t.kt < lim) lim = row + 1 - t.kt;
   if (causal == 2) {
-    const int64_t ks = kt / blk, c0 = kt - ks * blk;
-    const int64_t see = row_c + (ks <= row_w ? 1 : 0) - c0;
+    const int64_t see = row_c + (t.sk <= row_w ? 1 : 0) - (t.kt - t.s0);
     if (see < lim) lim = see;
   }
   return (int)(lim < 0 ? 0 : (lim > bn ? bn : lim));
@@ -251,7 +251,9 @@ struct PhaseClock {
 #endif
 };
 
-template <int D_>
+// CM: the causal order (0 none, 1 sequence, 2 striped), a template argument so
+// that each instance carries only its own mask code.
+template <int D_, int CM>
 __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
   using C = Bf16Fwd<D_>;
   constexpr int D = C::D, BN = C::BN, NKB = BN / 16, NKK = BN / 32, NKS = D / 32, NDB = D / 16;
@@ -283,8 +285,8 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
   for (int qb = 0; qb < 2; ++qb) {
     myrow[qb] = wrow0 + 16 * qb + l16;
     row_ok[qb] = myrow[qb] < jb.r1;
-    row_w[qb] = p.causal == 2 ? myrow[qb] / p.blk : 0;  // striped: shard, index
-    row_c[qb] = p.causal == 2 ? myrow[qb] - row_w[qb] * p.blk : 0;
+    row_w[qb] = CM == 2 ? myrow[qb] / p.blk : 0;  // striped: shard, index
+    row_c[qb] = CM == 2 ? myrow[qb] - row_w[qb] * p.blk : 0;
   }
   // B operand of S^T = K Q^T: Q row 16 qb + l16, head dims 32 ks + 8 q4 ..
   bf16x8 qreg[2][NKS];
@@ -401,18 +403,18 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
   };
   const float c2 = p.scale_log2;
   auto phase_softmax = [&](const TileIter& t) {
-    bool need_mask = (t.kt + BN > t.ke) || (p.causal == 1 && t.kt + BN - 1 > wrow0);
-    if (p.causal == 2)
+    bool need_mask = (t.kt + BN > t.ke) || (CM == 1 && t.kt + BN - 1 > wrow0);
+    if constexpr (CM == 2)
       need_mask = __builtin_amdgcn_ballot_w64(
-                      visible_prefix(t.kt, t.ke, 2, myrow[0], BN, p.blk, row_w[0], row_c[0]) < BN ||
-                      visible_prefix(t.kt, t.ke, 2, myrow[1], BN, p.blk, row_w[1], row_c[1]) < BN) != 0;
+                      visible_prefix(t, 2, myrow[0], BN, row_w[0], row_c[0]) < BN ||
+                      visible_prefix(t, 2, myrow[1], BN, row_w[1], row_c[1]) < BN) != 0;
     if (need_mask) {
       // the part of the key that depends on q4 is moved to the limit
       const int gk = kperm<D>(0, 4 * q4) - kperm<D>(0, 0);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int lim =
-            visible_prefix(t.kt, t.ke, p.causal, myrow[qb], BN, p.blk, row_w[qb], row_c[qb]) - gk;
+            visible_prefix(t, CM, myrow[qb], BN, row_w[qb], row_c[qb]) - gk;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -679,7 +681,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
   if (it.valid(jb)) load(it);
   while (it.valid(jb)) {
     // keys it.kt + j, j < lim, are visible to this row
-    const int lim = visible_prefix(it.kt, it.ke, p.causal, myrow, BN, p.blk, row_w, row_c);
+    const int lim = visible_prefix(it, p.causal, myrow, BN, row_w, row_c);
     __syncthreads();  // every read of the previous tile is done
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
@@ -758,10 +760,16 @@ hipError_t fwd_launch(FwdParams p, int dtype_bf16, hipStream_t st) {
   }
 #endif
   if (dtype_bf16) {
-    if (p.D == 128)
-      hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3(blocks), dim3(Bf16Fwd<128>::NT), 0, st, p);
-    else
-      hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3(blocks), dim3(Bf16Fwd<64>::NT), 0, st, p);
+    const dim3 g(blocks), b128(Bf16Fwd<128>::NT), b64(Bf16Fwd<64>::NT);
+    if (p.D == 128) {
+      if (p.causal == 2) hipLaunchKernelGGL((fwd_bf16_kernel<128, 2>), g, b128, 0, st, p);
+      else if (p.causal == 1) hipLaunchKernelGGL((fwd_bf16_kernel<128, 1>), g, b128, 0, st, p);
+      else hipLaunchKernelGGL((fwd_bf16_kernel<128, 0>), g, b128, 0, st, p);
+    } else {
+      if (p.causal == 2) hipLaunchKernelGGL((fwd_bf16_kernel<64, 2>), g, b64, 0, st, p);
+      else if (p.causal == 1) hipLaunchKernelGGL((fwd_bf16_kernel<64, 1>), g, b64, 0, st, p);
+      else hipLaunchKernelGGL((fwd_bf16_kernel<64, 0>), g, b64, 0, st, p);
+    }
   } else {
     if (p.D == 128)
       hipLaunchKernelGGL(fwd_f32_kernel<128>, dim3(blocks), dim3(256), 0, st, p);
