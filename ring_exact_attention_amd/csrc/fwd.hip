@@ -133,15 +133,16 @@ __device__ inline void store4<bf16>(bf16* dst, float a, float b, float c, float 
 // SIMD is in its MFMA phase while the other is in its VALU phase, so that
 // the matrix core and the vector ALU can work at the same time.  Barrier intervals
 // ("slots") are numbered from 0; group A runs
-//   slot 0: S(0);  slot 2j+1: softmax(j), load K(j+2);  slot 2j+2: PV(j) + S(j+1)
-// and group B runs the same sequence one slot later (loading V(j+2) in its
-// softmax slot).  K/V tiles rotate through three LDS buffers (tile j in buffer
-// j mod 3) and move from global memory to LDS directly (global_load_lds, no
+//   slot 0: S(0);  slot 2j+1: softmax(j), load K(j+3);  slot 2j+2: PV(j) + S(j+1)
+// and group B runs the same sequence one slot later (loading V(j+3) in its
+// softmax slot).  K/V tiles rotate through four LDS buffers (tile j in buffer
+// j mod 4) and move from global memory to LDS directly (global_load_lds, no
 // registers).  Tile j's K is read in slots 2j and 2j+1 and its V in slots
-// 2j+2 and 2j+3, so K(j+2) may land in slot 2j+1 (K(j-1) was last read in
-// slot 2j-1) and V(j+2) in slot 2j+2 (V(j-1) last read in slot 2j+1).  A
-// group waits for its loads of tile j+1 in its next softmax slot, before the
-// barrier after which the tile is read.
+// 2j+2 and 2j+3, so K(j+3) may land in slot 2j+1 (K(j-1) was last read in
+// slot 2j-1) and V(j+3) in slot 2j+2 (V(j-1) last read in slot 2j+1).  A
+// group waits for its loads of tile j+1 in its next softmax slot (those of
+// tile j+2 may stay in flight), before the barrier after which the tile is
+// read.
 
 template <int D_>
 struct Bf16Fwd {
@@ -157,7 +158,7 @@ struct Bf16Fwd {
   static constexpr int BS = 1024 + 32;
   static constexpr int K_TILE = NBK * BS, V_TILE = NBK * BS;  // bytes
   static constexpr int STAGE = K_TILE + V_TILE;
-  static constexpr int NBUF = 3;
+  static constexpr int NBUF = 4;
   static constexpr int KC = NBK / 4;  // blocks per wave and tile (four waves per group)
   static_assert(NBH * RPB == 32 && KC * 4 == NBK && NBH >= 4, "tile geometry");
 };
@@ -483,20 +484,23 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     lsum[1] += ts[1];
   };
 
-  // ---- prologue: tile 0 into buffer 0, tile 1 in flight.  A job without
-  // visible tiles skips the prologue and the loop altogether (the condition is
-  // uniform over the workgroup), so both groups always pass the same barriers.
-  TileIter tw = tv;  // latest tile this thread's group has loaded
+  // ---- prologue: tile 0 into buffer 0, tiles 1 and 2 in flight.  A job
+  // without visible tiles skips the prologue and the loop altogether (the
+  // condition is uniform over the workgroup), so both groups always pass the
+  // same barriers.
+  TileIter tw = tv;  // next tile this thread's group loads
+  int issued = 0;    // tiles loaded so far (tile i into buffer i mod NBUF)
   PhaseClock clk;
   if (tv.valid(jb)) {
-    dma_tile(tw, 0);
-    tw.advance(p, jb, BN);
-    if (tw.valid(jb)) {
-      dma_tile(tw, 1);
-      wait_vm<C::KC>();  // tile 0 has landed, tile 1 is in flight
-    } else {
-      wait_vm<0>();
+    for (int i = 0; i < 3 && tw.valid(jb); ++i) {
+      dma_tile(tw, i);
+      tw.advance(p, jb, BN);
+      ++issued;
     }
+    // tile 0 has landed; the loads of the tiles after it may still be in flight
+    if (issued == 3) wait_vm<2 * C::KC>();
+    else if (issued == 2) wait_vm<C::KC>();
+    else wait_vm<0>();
     slot_barrier();
     if (!groupB) {
       phase_s(0);  // slot 0
@@ -522,7 +526,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
     int j = 0;
     clk.start();
     while (tv.valid(jb)) {
-      const int cur = j % 3, nxt = (j + 1) % 3;
+      const int cur = j % C::NBUF, nxt = (j + 1) % C::NBUF;
       phase_softmax(tv);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
@@ -532,10 +536,14 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdParams p) {
       pin(lsum[0]);
       pin(lsum[1]);
       clk.after_valu();
-      if (tw.valid(jb)) {  // tile j+1 has landed (published by the barrier below); load tile j+2
-        wait_vm<0>();
+      // tile j+1 has landed (published by the barrier below; tile j+2 may still
+      // be in flight); load tile j+3
+      if (issued > j + 2) wait_vm<C::KC>();
+      else wait_vm<0>();
+      if (tw.valid(jb)) {
+        dma_tile(tw, (j + 3) % C::NBUF);
         tw.advance(p, jb, BN);
-        if (tw.valid(jb)) dma_tile(tw, (j + 2) % 3);
+        ++issued;
       }
       clk.after_staging();
       slot_barrier();
