@@ -754,7 +754,8 @@ def main():
             roofline = {"bound": "mfma", "achieved": round(achieved, 2),
                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
-        roofline.update({"kernel": f"fwd_bf16_kernel<{w.D}>", "launches_per_step": launches,
+        cm = 2 if causal == "striped" else (1 if causal else 0)  # the kernel's causal instance
+        roofline.update({"kernel": f"fwd_bf16_kernel<{w.D}, {cm}>", "launches_per_step": launches,
                          "kernel_ms_per_launch": round(kernel_ms, 4),
                          "other_ms_per_step": round(ms - fwd_ms, 4),
                          "mfma_busy_profiled": busy, "clock_ghz_profiled": clock})
